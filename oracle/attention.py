@@ -1,0 +1,84 @@
+"""CPU float64 oracle for the dense (non-causal) attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call this
+module; only the tests, the package's smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP kernels.
+
+What it computes is the plain definition of softmax attention, written out
+directly, materialising every full row of the score matrix:
+
+    s_ij   = scale * sum_d q_id k_jd                      (scores)
+    m_i    = max_j s_ij                                   (row maximum)
+    e_ij   = exp(s_ij - m_i)
+    l_i    = sum_j e_ij                                   (row sum)
+    o_id   = (sum_j e_ij v_jd) / l_i                      (normalised output)
+    lse_i  = m_i + ln l_i                                 (natural-log log-sum-exp)
+
+Sources.  The per-(batch, head, query-tile) work split, the S = Q·Kᵀ / softmax
+/ P·V sections and the final division by the row sum follow "B200 Attention
+Kernel from Scratch to Near-SOTA in 60 Diagrams", Chapter 1, "ii. Work
+Parallelization" and "B) Online Softmax (explaining S->P)".  The
+materialise-then-reduce shape (scores for a whole row, then max, then
+exp-and-sum, then normalise) is the unfused baseline of "Learning
+FlashAttention the Hard Way - Part 2", "Move 0 - Scalar Streaming Kernel".
+The log-sum-exp residual is kept in natural-log units as "Attention for sm90,
+Line by Line" describes in "Why does the kernel use exp2 rather than exp?".
+
+The online (tile-by-tile) softmax of the GPU path is exact in real arithmetic,
+so the oracle does not emulate it: it evaluates the definition once per row in
+float64.  Rows are processed in blocks only to bound memory; every row always
+sees all S keys.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["attention_forward", "attention_rows"]
+
+
+def _as_f64(x) -> np.ndarray:
+    a = np.asarray(x, dtype=np.float64)
+    if a.ndim != 4:
+        raise ValueError("expected a [B, H, S, D] array")
+    return a
+
+
+def _rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float):
+    """Attention of the query rows ``qh`` [R, D] against one head's keys/values [S, D]."""
+    s = scale * (qh @ kh.T)                 # [R, S] scores
+    m = s.max(axis=1, keepdims=True)        # [R, 1] row maxima
+    e = np.exp(s - m)                       # [R, S]
+    l = e.sum(axis=1, keepdims=True)        # [R, 1] row sums
+    o = (e @ vh) / l                        # [R, D]
+    lse = m[:, 0] + np.log(l[:, 0])         # [R]
+    return o, lse
+
+
+def attention_forward(q, k, v, scale: float, row_block: int = 1024):
+    """Full forward over [B, H, S, D] inputs.  Returns (o [B,H,S,D], lse [B,H,S]) in float64."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, S, D = q.shape
+    if k.shape != (B, H, S, D) or v.shape != (B, H, S, D):
+        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    o = np.empty((B, H, S, D), dtype=np.float64)
+    lse = np.empty((B, H, S), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, S, row_block):
+                r1 = min(S, r0 + row_block)
+                o[b, h, r0:r1], lse[b, h, r0:r1] = _rows(q[b, h, r0:r1], k[b, h], v[b, h], scale)
+    return o, lse
+
+
+def attention_rows(q, k, v, scale: float, b: int, h: int, rows):
+    """The same definition for selected query rows of one (b, h) only, each against all keys.
+
+    Used to check large problems on a sample of output rows.  Returns
+    (o [len(rows), D], lse [len(rows)]) in float64.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    qh = np.asarray(q[b, h], dtype=np.float64)[rows]
+    kh = np.asarray(k[b, h], dtype=np.float64)
+    vh = np.asarray(v[b, h], dtype=np.float64)
+    return _rows(qh, kh, vh, scale)

@@ -1,0 +1,147 @@
+"""CPU tests of the float64 oracle against its pins, plus planted-mistake checks.
+
+The planted mistakes replace the oracle's per-row kernel with a copy carrying
+one plausible slip (a dropped term, a wrong sign, a transposed operand, a
+wrong axis, a wrong log base ...).  Every such copy must fail at least one pin,
+which shows the pins constrain every step of the definition.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.attention as oa
+from oracle import attention_forward, attention_rows
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(attention_forward)
+
+
+def test_rows_api_matches_full_forward():
+    rng = np.random.default_rng(3)
+    q, k, v = (rng.standard_normal((2, 3, 70, 16)) for _ in range(3))
+    o, lse = attention_forward(q, k, v, 0.25, row_block=16)
+    rows = [0, 5, 33, 69]
+    o_r, l_r = attention_rows(q, k, v, 0.25, 1, 2, rows)
+    np.testing.assert_allclose(o_r, o[1, 2, rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_r, lse[1, 2, rows], rtol=0, atol=1e-13)
+
+
+def test_row_blocking_does_not_change_result():
+    rng = np.random.default_rng(4)
+    q, k, v = (rng.standard_normal((1, 2, 130, 8)) for _ in range(3))
+    a = attention_forward(q, k, v, 0.5, row_block=7)
+    b = attention_forward(q, k, v, 0.5, row_block=4096)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-14)
+
+
+def test_rejects_mismatched_shapes():
+    with pytest.raises(ValueError):
+        attention_forward(np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 5, 2)), np.zeros((1, 1, 5, 2)), 1.0)
+
+
+# --- planted mistakes -------------------------------------------------------
+
+def _m_transposed_scores(qh, kh, vh, scale):
+    s = scale * (kh @ qh.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
+
+
+def _m_no_scale(qh, kh, vh, scale):
+    return oa.__dict__["_orig_rows"](qh, kh, vh, 1.0)
+
+
+def _m_sign(qh, kh, vh, scale):
+    return oa.__dict__["_orig_rows"](qh, kh, vh, -scale)
+
+
+def _m_wrong_axis(qh, kh, vh, scale):
+    s = scale * (qh @ kh.T)
+    m = s.max(axis=0, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=0, keepdims=True)
+    o = (e / l) @ vh
+    return o, np.log(np.exp(s).sum(axis=1))
+
+
+def _m_no_max_subtraction(qh, kh, vh, scale):
+    s = scale * (qh @ kh.T)
+    e = np.exp(s)
+    l = e.sum(axis=1, keepdims=True)
+    return (e @ vh) / l, np.log(l[:, 0])
+
+
+def _m_lse_without_max(qh, kh, vh, scale):
+    o, lse = oa.__dict__["_orig_rows"](qh, kh, vh, scale)
+    m = (scale * (qh @ kh.T)).max(axis=1)
+    return o, lse - m
+
+
+def _m_lse_base2(qh, kh, vh, scale):
+    o, lse = oa.__dict__["_orig_rows"](qh, kh, vh, scale)
+    return o, lse / np.log(2.0)
+
+
+def _m_no_normalisation(qh, kh, vh, scale):
+    s = scale * (qh @ kh.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return e @ vh, m[:, 0] + np.log(l[:, 0])
+
+
+def _m_dropped_last_key_in_sum(qh, kh, vh, scale):
+    s = scale * (qh @ kh.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e[:, :-1].sum(axis=1, keepdims=True) if e.shape[1] > 1 else e.sum(axis=1, keepdims=True)
+    return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
+
+
+def _m_reversed_values(qh, kh, vh, scale):
+    return oa.__dict__["_orig_rows"](qh, kh, vh[::-1], scale)
+
+
+def _m_keys_used_as_values(qh, kh, vh, scale):
+    return oa.__dict__["_orig_rows"](qh, kh, kh, scale)
+
+
+def _m_off_by_one_key(qh, kh, vh, scale):
+    s = scale * (qh @ np.roll(kh, 1, axis=0).T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
+
+
+def _m_exp2_instead_of_exp(qh, kh, vh, scale):
+    s = scale * (qh @ kh.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp2(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
+
+
+MUTANTS = [_m_transposed_scores, _m_no_scale, _m_sign, _m_wrong_axis, _m_no_max_subtraction,
+           _m_lse_without_max, _m_lse_base2, _m_no_normalisation, _m_dropped_last_key_in_sum,
+           _m_reversed_values, _m_keys_used_as_values, _m_off_by_one_key, _m_exp2_instead_of_exp]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
+def test_planted_mistake_fails_some_pin(mutant, monkeypatch):
+    monkeypatch.setitem(oa.__dict__, "_orig_rows", oa._rows)
+    monkeypatch.setattr(oa, "_rows", mutant)
+    failed = []
+    with np.errstate(all="ignore"):
+        for pin in P.ALL_PINS:
+            try:
+                pin(oa.attention_forward)
+            except (AssertionError, ValueError, FloatingPointError):
+                failed.append(pin.__name__)
+    assert failed, f"planted mistake {mutant.__name__} passed every pin"
