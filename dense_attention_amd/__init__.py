@@ -1,0 +1,191 @@
+"""dense_attention_amd: fused dense attention forward on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libattn.so`` (declared in
+``include/attn.h``).  It only marshals arguments: every step of the attention
+forward runs in the library's HIP kernels.  PyTorch supplies device memory and
+streams.  There is no fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = [
+    "ATTN_F16", "ATTN_BF16", "AttnError", "attn_fwd", "attn_fwd_ex", "attn_get_config",
+    "attn_variants", "attn_strerror", "library_path", "load_library",
+]
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+
+STATUS = {
+    0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_DTYPE", -3: "ATTN_ERR_SHAPE",
+    -4: "ATTN_ERR_ALIGN", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_DEVICE", -7: "ATTN_ERR_LAUNCH",
+    -8: "ATTN_ERR_ARG",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libattn.so")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        super().__init__(f"{name}: {detail}" if detail else name)
+
+
+class attn_fwd_options(ctypes.Structure):
+    _fields_ = [("rescale_threshold", ctypes.c_float), ("variant", ctypes.c_int),
+                ("grid", ctypes.c_int), ("reserved", ctypes.c_int * 4)]
+
+
+class attn_config(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("waves", ctypes.c_int), ("stages", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("work_items", ctypes.c_int), ("grid", ctypes.c_int),
+                ("workgroups_per_cu", ctypes.c_int), ("num_cus", ctypes.c_int)]
+
+
+def load_library(path: str | None = None):
+    """Loads libattn.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or library_path()
+        if not os.path.exists(p):
+            raise ImportError(f"{p} is missing: build it with `python -m dense_attention_amd.build`")
+        lib = ctypes.CDLL(p)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.attn_fwd.restype = i
+        lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
+                                    ctypes.POINTER(attn_fwd_options)]
+        lib.attn_fwd_ex.restype = i
+        lib.attn_get_config.argtypes = [i, i, i, i, i, ctypes.POINTER(attn_fwd_options),
+                                        ctypes.POINTER(attn_config)]
+        lib.attn_get_config.restype = i
+        lib.attn_variant_count.argtypes = []
+        lib.attn_variant_count.restype = i
+        ip = ctypes.POINTER(ctypes.c_int)
+        lib.attn_variant_info.argtypes = [i, ip, ip, ip, ip, ip, ip, ip]
+        lib.attn_variant_info.restype = i
+        lib.attn_strerror.argtypes = [i]
+        lib.attn_strerror.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def attn_strerror(status: int) -> str:
+    return load_library().attn_strerror(status).decode()
+
+
+def _check(lib, status: int):
+    if status != 0:
+        raise AttnError(status, lib.attn_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def _options(rescale_threshold, variant, grid):
+    opts = attn_fwd_options()
+    opts.rescale_threshold = -1.0 if rescale_threshold is None else float(rescale_threshold)
+    opts.variant = int(variant)
+    opts.grid = int(grid)
+    return opts
+
+
+def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_lse=True,
+                rescale_threshold=None, variant=0, grid=0):
+    """O = softmax(scale·Q·Kᵀ)·V (and the fp32 LSE) for contiguous [B, H, S, D] tensors.
+
+    ``o`` and ``lse`` are allocated with torch when not given.  ``stream`` is a
+    ``torch.cuda.Stream`` (default: the current stream).  Returns (o, lse);
+    lse is None when ``return_lse`` is false and no buffer was passed.
+    """
+    import torch
+
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    B, H, S, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, S, D]")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous tensor like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    opts = _options(rescale_threshold, variant, grid)
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr() if lse is not None else None, B, H, S, D,
+                             float(scale), dt, stream.cuda_stream, ctypes.byref(opts))
+    _check(lib, st)
+    return o, lse
+
+
+def attn_fwd(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_lse=True):
+    """The library's default attention forward; see attn_fwd_ex."""
+    return attn_fwd_ex(q, k, v, o, lse, scale, stream=stream, return_lse=return_lse)
+
+
+def attn_get_config(B, H, S, D, dtype, *, rescale_threshold=None, variant=0, grid=0) -> dict:
+    """Launch configuration for the current device (needs a gfx950 GPU)."""
+    lib = load_library()
+    code = dtype if isinstance(dtype, int) else _dtype_code_from_torch(dtype)
+    out = attn_config()
+    opts = _options(rescale_threshold, variant, grid)
+    _check(lib, lib.attn_get_config(B, H, S, D, code, ctypes.byref(opts), ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in attn_config._fields_}
+
+
+def _dtype_code_from_torch(dtype) -> int:
+    import torch
+    return {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}[dtype]
+
+
+def attn_variants() -> list:
+    """All tile variants compiled into the library (host only)."""
+    lib = load_library()
+    out = []
+    for idx in range(lib.attn_variant_count()):
+        vals = [ctypes.c_int() for _ in range(7)]
+        _check(lib, lib.attn_variant_info(idx, *[ctypes.byref(x) for x in vals]))
+        keys = ["id", "head_dim", "dtype", "block_m", "block_n", "waves", "stages"]
+        out.append({kk: x.value for kk, x in zip(keys, vals)})
+    return out

@@ -1,0 +1,157 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+rejects invalid arguments before touching a device (no compute calls here)."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_attention_amd as da
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(da.library_path()):
+        from dense_attention_amd import build
+        build.build()
+    return da.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["attn_fwd", "attn_fwd_ex", "attn_get_config", "attn_variant_count",
+              "attn_variant_info", "attn_strerror", "attn_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", da.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_gfx950_code_object(lib):
+    data = open(da.library_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+def _call(lib, q=0x1000, k=0x2000, v=0x3000, o=0x4000, lse=None, B=1, H=1, S=16, D=64,
+          scale=0.125, dtype=1, opts=None):
+    if opts is None:
+        return lib.attn_fwd(q, k, v, o, lse, B, H, S, D, scale, dtype, None)
+    return lib.attn_fwd_ex(q, k, v, o, lse, B, H, S, D, scale, dtype, None, ctypes.byref(opts))
+
+
+def test_rejects_bad_dtype(lib):
+    assert _call(lib, dtype=2) == -2
+    assert _call(lib, dtype=-1) == -2
+
+
+def test_rejects_bad_shapes(lib):
+    assert _call(lib, S=-1) == -3
+    assert _call(lib, B=-2) == -3
+    assert _call(lib, D=96) == -3
+    assert _call(lib, D=0) == -3
+    assert _call(lib, S=1 << 24, D=128) == -3          # S*D overflows 31 bits
+    assert _call(lib, B=1 << 12, H=1 << 12, S=1 << 8) == -3
+
+
+def test_rejects_non_finite_scale(lib):
+    assert _call(lib, scale=float("nan")) == -5
+    assert _call(lib, scale=float("inf")) == -5
+
+
+def test_empty_problem_is_ok_without_pointers(lib):
+    assert _call(lib, q=None, k=None, v=None, o=None, B=0) == 0
+    assert _call(lib, q=None, k=None, v=None, o=None, S=0) == 0
+    assert _call(lib, q=None, k=None, v=None, o=None, H=0, D=128, dtype=0) == 0
+
+
+def test_rejects_null_and_misaligned(lib):
+    assert _call(lib, q=None) == -1
+    assert _call(lib, o=None) == -1
+    assert _call(lib, k=0x2008) == -4
+    assert "16-byte" in lib.attn_last_error().decode()
+    assert _call(lib, lse=0x5002) == -4
+    assert "4-byte" in lib.attn_last_error().decode()
+
+
+def test_rejects_bad_options(lib):
+    o = da.attn_fwd_options()
+    o.rescale_threshold = -1.0
+    o.reserved[2] = 1
+    assert _call(lib, opts=o) == -8
+    o = da.attn_fwd_options()
+    o.rescale_threshold = 100.0
+    assert _call(lib, opts=o) == -8
+    o = da.attn_fwd_options()
+    o.rescale_threshold = float("nan")
+    assert _call(lib, opts=o) == -8
+    o = da.attn_fwd_options()
+    o.variant = 12345
+    assert _call(lib, opts=o) == -8
+    o = da.attn_fwd_options()
+    o.grid = -3
+    assert _call(lib, opts=o) == -8
+
+
+def test_variant_must_match_head_dim_and_dtype(lib):
+    for var in da.attn_variants():
+        other_d = 64 if var["head_dim"] == 128 else 128
+        o = da.attn_fwd_options()
+        o.variant = var["id"]
+        o.rescale_threshold = -1.0
+        assert _call(lib, D=other_d, dtype=var["dtype"], opts=o) == -8
+        assert _call(lib, D=var["head_dim"], dtype=1 - var["dtype"], opts=o) == -8
+
+
+def test_variant_table(lib):
+    vs = da.attn_variants()
+    assert len(vs) == lib.attn_variant_count() >= 4
+    ids = [v["id"] for v in vs]
+    assert len(set(ids)) == len(ids)
+    for v in vs:
+        assert v["head_dim"] in (64, 128)
+        assert v["dtype"] in (0, 1)
+        assert v["block_m"] == 32 * v["waves"] * (v["block_m"] // (32 * v["waves"]))
+        assert v["block_n"] % 64 == 0
+    for d in (64, 128):
+        for dt in (0, 1):
+            assert any(v["head_dim"] == d and v["dtype"] == dt for v in vs)
+    assert lib.attn_variant_info(len(vs), None, None, None, None, None, None, None) == -8
+
+
+def test_strerror_covers_every_status(lib):
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 7]:
+        s = lib.attn_strerror(code)
+        assert s is not None and len(s) > 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        da.load_library(str(tmp_path / "missing.so"))
+
+
+def test_binding_validates_before_calling(lib):
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        da.attn_fwd(q, q, q)          # CPU tensors are rejected before any library call
+    with pytest.raises(TypeError):
+        da._dtype_code(torch.zeros(1, dtype=torch.float32))
+    assert math.isclose(1.0 / math.sqrt(64), 0.125)

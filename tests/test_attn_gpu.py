@@ -1,0 +1,243 @@
+"""GPU parity tests: the HIP attention forward, called through the C ABI, against
+the float64 CPU oracle on the same seeded inputs.
+
+Bar (O against the unrounded float64 oracle, LSE absolute):
+    max |dO| <= 2e-2, mean |dO| <= 2e-3, max |dLSE| <= 1e-3.
+Full element-wise comparison where the oracle finishes in seconds; sampled
+rows (each computed by the oracle against all keys) at the full benchmark
+sizes, in the launch configuration the benchmark times.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dense_attention_amd as da
+import workloads as W
+from oracle import attention_forward, attention_rows
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    da.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_run(q, k, v, scale, **kw):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = da.attn_fwd_ex(qd, kd, vd, scale=scale, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_full(o, lse, q, k, v, scale, tag=""):
+    ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale)
+    go = o.cpu().to(torch.float64).numpy()
+    err = np.abs(go - ro)
+    say(f"  {tag} O max {err.max():.3e} mean {err.mean():.3e}" +
+        (f" LSE max {np.abs(lse.cpu().double().numpy() - rl).max():.3e}" if lse is not None else ""))
+    assert np.all(np.isfinite(go))
+    assert err.max() <= O_MAX and err.mean() <= O_MEAN, tag
+    if lse is not None:
+        gl = lse.cpu().to(torch.float64).numpy()
+        assert np.all(np.isfinite(gl))
+        assert np.abs(gl - rl).max() <= LSE_MAX, tag
+    return ro, rl
+
+
+def variants_for(D, dtype):
+    code = da.ATTN_F16 if dtype == "fp16" else da.ATTN_BF16
+    return [v["id"] for v in da.attn_variants() if v["head_dim"] == D and v["dtype"] == code]
+
+
+# --- the five workloads ------------------------------------------------------
+
+def test_config_small_fp16_all_variants():
+    w = W.CONFIGS[0]
+    q, k, v = W.workload_qkv(w)
+    for var in [0] + variants_for(w.D, w.dtype):
+        say(f"{w.name} variant {var}")
+        o, lse = gpu_run(q, k, v, w.scale, variant=var)
+        check_full(o, lse, q, k, v, w.scale, tag=f"{w.name}/v{var}")
+
+
+def test_config_s4096_d64_fp16_full():
+    w = W.CONFIGS[1]
+    q, k, v = W.workload_qkv(w)
+    say(f"{w.name} default launch")
+    o, lse = gpu_run(q, k, v, w.scale)
+    check_full(o, lse, q, k, v, w.scale, tag=w.name)
+
+
+def _sample_rows(S, n, rng, tile=128):
+    rows = set(rng.choice(S, size=n, replace=False).tolist())
+    rows |= {0, 1, tile - 1, tile, S // 2, S - tile, S - 1}
+    return np.array(sorted(r for r in rows if 0 <= r < S))
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4], ids=lambda i: W.CONFIGS[i].name)
+def test_config_hd128_bf16_sampled(idx):
+    w = W.CONFIGS[idx]
+    q, k, v = W.workload_qkv(w)
+    say(f"{w.name} default launch (the benchmark's)")
+    o, lse = gpu_run(q, k, v, w.scale)
+    go = o.cpu()
+    gl = lse.cpu().double().numpy()
+    assert torch.isfinite(go.float()).all() and np.all(np.isfinite(gl))
+    qn, kn, vn = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    rng = np.random.default_rng(100 + idx)
+    pairs = {(0, 0), (w.B - 1, w.H - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.H)))
+                                              for _ in range(4)}
+    worst_o = worst_l = 0.0
+    errs = []
+    for (b, h) in sorted(pairs):
+        rows = _sample_rows(w.S, 48, rng)
+        ro, rl = attention_rows(qn, kn, vn, w.scale, b, h, rows)
+        e = np.abs(go[b, h, rows].double().numpy() - ro)
+        errs.append(e)
+        worst_o = max(worst_o, e.max())
+        worst_l = max(worst_l, np.abs(gl[b, h, rows] - rl).max())
+    allerr = np.concatenate([e.ravel() for e in errs])
+    say(f"  sampled O max {worst_o:.3e} mean {allerr.mean():.3e} LSE max {worst_l:.3e}")
+    assert worst_o <= O_MAX and allerr.mean() <= O_MEAN and worst_l <= LSE_MAX
+    # Property at any size: each output lies in the convex hull of its head's V rows.
+    vd = v.cuda().float()
+    lo = vd.amin(dim=2, keepdim=True).cpu()
+    hi = vd.amax(dim=2, keepdim=True).cpu()
+    of = go.float()
+    assert bool(((of >= lo - 1e-2) & (of <= hi + 1e-2)).all())
+
+
+# --- edge cases -----------------------------------------------------------------
+
+RAGGED = [1, 2, 31, 64, 65, 100, 127, 129, 200, 257, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_ragged_lengths_all_variants(D, dtype):
+    for S in RAGGED:
+        q, k, v = W.gaussian_qkv(2, 3, S, D, dtype, seed=1000 + S)
+        scale = 1.0 / math.sqrt(D)
+        for var in variants_for(D, dtype):
+            say(f"ragged S={S} D={D} {dtype} variant {var}")
+            o, lse = gpu_run(q, k, v, scale, variant=var)
+            check_full(o, lse, q, k, v, scale, tag=f"S{S}/D{D}/{dtype}/v{var}")
+
+
+def test_empty_problem_launches_nothing():
+    q = torch.zeros(0, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = da.attn_fwd(q, q, q)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape and lse.shape == (0, 2, 16)
+    q = torch.zeros(1, 1, 0, 128, dtype=torch.float16, device="cuda")
+    o, lse = da.attn_fwd(q, q, q)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+
+
+def test_lse_pointer_may_be_null():
+    q, k, v = W.gaussian_qkv(1, 2, 300, 128, "bf16", seed=7)
+    o, lse = gpu_run(q, k, v, 1 / math.sqrt(128), return_lse=False)
+    assert lse is None
+    check_full(o, None, q, k, v, 1 / math.sqrt(128), tag="lse=NULL")
+
+
+def test_zero_query_gives_mean_of_v_and_ln_s():
+    for D, dtype, S in [(64, "fp16", 384), (128, "bf16", 1000)]:
+        _, k, v = W.gaussian_qkv(1, 2, S, D, dtype, seed=21)
+        q = torch.zeros_like(k)
+        o, lse = gpu_run(q, k, v, 1 / math.sqrt(D))
+        mean_v = W.to_f64(v).mean(axis=2, keepdims=True)
+        err = np.abs(o.cpu().double().numpy() - mean_v)
+        say(f"  Q=0 D={D} S={S} O max {err.max():.3e}")
+        assert err.max() <= O_MAX and err.mean() <= O_MEAN
+        assert np.abs(lse.cpu().double().numpy() - math.log(S)).max() <= LSE_MAX
+
+
+def test_constant_v():
+    q, k, _ = W.gaussian_qkv(1, 2, 777, 128, "bf16", seed=22)
+    c = torch.linspace(-2, 2, 128).to(torch.bfloat16)
+    v = c.expand(1, 2, 777, 128).contiguous()
+    o, _ = gpu_run(q, k, v, 1 / math.sqrt(128))
+    err = (o.cpu().double() - c.double()).abs()
+    assert err.max() <= O_MAX and err.mean() <= O_MEAN
+
+
+def test_scale_zero_negative_and_sharp():
+    q, k, v = W.gaussian_qkv(1, 2, 333, 64, "bf16", seed=23)
+    for scale in [0.0, -0.125, 1.0]:
+        say(f"scale {scale}")
+        o, lse = gpu_run(q, k, v, scale)
+        check_full(o, lse, q, k, v, scale, tag=f"scale={scale}")
+
+
+@pytest.mark.parametrize("thr", [0.0, 8.0, 64.0])
+def test_forced_rebase_thresholds(thr):
+    q, k, v = W.forced_rebase_qkv()
+    o, lse = gpu_run(q, k, v, 1 / math.sqrt(64), rescale_threshold=thr)
+    check_full(o, lse, q, k, v, 1 / math.sqrt(64), tag=f"threshold {thr}")
+
+
+def test_tile_signature_exact():
+    """Q = 0 and a one-hot V per 64-key tile: every stale, skipped or doubled tile shows."""
+    for D, dtype in [(128, "bf16"), (64, "fp16")]:
+        S = 4096
+        for var in variants_for(D, dtype):
+            v = W.tile_signature_v(1, 2, S, D, dtype, tile=64)
+            q = torch.zeros_like(v)
+            k = W.gaussian_qkv(1, 2, S, D, dtype, seed=24)[1]
+            o, lse = gpu_run(q, k, v, 1 / math.sqrt(D), variant=var)
+            expect = np.zeros(D)
+            cols = (np.arange(S) // 64) % D
+            np.add.at(expect, cols, 1.0 / S)
+            err = np.abs(o.cpu().double().numpy() - expect)
+            say(f"  tile signature D={D} variant {var}: max err {err.max():.3e}")
+            assert err.max() <= 1e-6
+
+
+def test_grid_sizes_give_identical_results():
+    q, k, v = W.gaussian_qkv(2, 4, 1111, 128, "bf16", seed=25)
+    ref, ref_l = gpu_run(q, k, v, 0.088)
+    for g in [1, 3, 8, 13, 64]:
+        say(f"grid {g}")
+        o, lse = gpu_run(q, k, v, 0.088, grid=g)
+        assert torch.equal(o, ref) and torch.equal(lse, ref_l), g
+
+
+def test_non_default_stream():
+    q, k, v = W.gaussian_qkv(1, 4, 512, 64, "fp16", seed=26)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        o, lse = da.attn_fwd(qd, kd, vd, stream=s)
+    s.synchronize()
+    check_full(o, lse, q, k, v, 1 / math.sqrt(64), tag="side stream")
+
+
+def test_long_sequence_sampled():
+    S = 32768 + 17
+    q, k, v = W.gaussian_qkv(1, 1, S, 128, "bf16", seed=27)
+    o, lse = gpu_run(q, k, v, 1 / math.sqrt(128))
+    rng = np.random.default_rng(27)
+    rows = _sample_rows(S, 64, rng)
+    ro, rl = attention_rows(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / math.sqrt(128), 0, 0, rows)
+    e = np.abs(o[0, 0].cpu()[rows].double().numpy() - ro)
+    say(f"  S={S} sampled O max {e.max():.3e}")
+    assert e.max() <= O_MAX and e.mean() <= O_MEAN
+    assert np.abs(lse[0, 0].cpu()[rows].double().numpy() - rl).max() <= LSE_MAX
