@@ -1,0 +1,199 @@
+"""Benchmark of the fused dense attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one attn_fwd call over the whole workload (all heads, all query
+tiles), inputs already resident in device memory.  Prints ONE JSON line.
+
+* value / metric: attention-forward throughput, 4·B·H·S²·D / t, in TFLOP/s.
+* roofline: the kernel is MFMA bound (dense bf16 contraction); achieved is the
+  algorithmic FLOP per launch over the average launch duration measured with
+  HIP events on the launch stream over the timed region; peak is MI355X's dense
+  bf16 MFMA figure.  traffic is the HBM bytes per launch measured by rocprofv3
+  counters (see profiles/), reported only while the kernel sources still match
+  the ones the counters were taken on.
+* cpu_baseline: the float64 CPU oracle timed on a bounded sample (whole query
+  rows of one head) of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn-fwd TFLOP/s (4BHS²D/t) + % bf16 MFMA peak, hd128 bf16 S=4K/8K/16K"
+DEFAULT_WORKLOAD = "b2_h16_s8192_d128_bf16"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense MFMA, no sparsity
+KERNEL_SOURCES = ["dense_attention_amd/csrc/attn_fwd_kernel.h", "dense_attention_amd/csrc/attn_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if they match these sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, rows: int):
+    """Times the float64 oracle on `rows` whole query rows of head (0, 0)."""
+    import numpy as np
+    import threadpoolctl
+    import workloads as W
+    from oracle import attention_rows
+
+    qn = W.to_f64(q[:1, :1])
+    kn = W.to_f64(k[:1, :1])
+    vn = W.to_f64(v[:1, :1])
+    sel = np.arange(rows)
+    t0 = time.perf_counter()
+    attention_rows(qn, kn, vn, w.scale, 0, 0, sel)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * rows * w.S * w.D
+    blas = [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+            if p.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{rows} query rows x {w.S} keys of head (0,0), D={w.D}, float64 numpy "
+                   f"(BLAS matmul on {cores} threads, exp single-threaded); {dt:.1f} s on "
+                   f"{os.cpu_count()} visible CPUs"),
+    }
+
+
+def copy_calibration(args):
+    """A plain device-to-device copy of known size (reads N bytes, writes N bytes)."""
+    import torch
+    n = args.copy_mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    t = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "steps": args.steps,
+                      "seconds_per_copy": t, "GB_per_s": 2 * n / t / 1e9}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="query rows of the oracle's CPU-baseline sample (0 skips it)")
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many MiB "
+                         "(calibrates the HBM byte counters of rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the attention forward runs on one "
+              "device's share; no multi-GPU path). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_attention_amd as da
+    import workloads as W
+
+    if args.copy_mib > 0:
+        return copy_calibration(args)
+
+    w = W.BY_NAME[args.workload]
+    q, k, v = W.workload_qkv(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        da.attn_fwd_ex(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps      # average launch duration
+    step_s = wall / args.steps
+
+    flops = w.flops
+    value = flops / step_s / 1e12
+    achieved = flops / kernel_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    cfg = da.attn_get_config(w.B, w.H, w.S, w.D, q.dtype, variant=args.variant)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: iid N(0,1) q/k/v from numpy PCG64 seed, rounded to dtype",
+        "config": dict(w.as_dict(), kernel=cfg),
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(w.name),
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_rows > 0:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(args.cpu_rows, w.S))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

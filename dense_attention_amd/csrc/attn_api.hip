@@ -29,18 +29,23 @@ int fail(int status, const char* detail) {
   return status;
 }
 
-typedef hipError_t (*launch_fn)(const Params&, int grid, hipStream_t stream);
+typedef hipError_t (*launch_fn)(const Params&, bool neg, int grid, hipStream_t stream);
 typedef hipError_t (*occ_fn)(int* blocks_per_cu);
 
+// Negative score multipliers use a separate instantiation (the running
+// maximum of c·s is then taken over min(s)).
 template <class T, class TL>
-hipError_t launch_impl(const Params& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL>), dim3(grid), dim3(TL::NT), 0, stream, p);
+hipError_t launch_impl(const Params& p, bool neg, int grid, hipStream_t stream) {
+  if (neg)
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, true>), dim3(grid), dim3(TL::NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, false>), dim3(grid), dim3(TL::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 template <class T, class TL>
 hipError_t occupancy_impl(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attn::attn_fwd_kernel<T, TL>,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attn::attn_fwd_kernel<T, TL, false>,
                                                        TL::NT, 0);
 }
 
@@ -66,14 +71,18 @@ constexpr Variant make_variant(int id) {
 // Tile variants: ids are stable; the first matching entry for (D, dtype) in
 // kDefaults is the library's choice.
 const Variant kVariants[] = {
-    make_variant<BF16, ATTN_BF16, Tile<128, 64, 4, 1>>(1),
-    make_variant<F16, ATTN_F16, Tile<128, 64, 4, 1>>(2),
+    make_variant<BF16, ATTN_BF16, Tile<128, 64, 8, 1>>(1),
+    make_variant<F16, ATTN_F16, Tile<128, 64, 8, 1>>(2),
     make_variant<BF16, ATTN_BF16, Tile<64, 64, 4, 1>>(3),
     make_variant<F16, ATTN_F16, Tile<64, 64, 4, 1>>(4),
-    make_variant<BF16, ATTN_BF16, Tile<128, 128, 4, 1>>(5),
-    make_variant<F16, ATTN_F16, Tile<128, 128, 4, 1>>(6),
-    make_variant<BF16, ATTN_BF16, Tile<64, 128, 4, 1>>(7),
-    make_variant<F16, ATTN_F16, Tile<64, 128, 4, 1>>(8),
+    make_variant<BF16, ATTN_BF16, Tile<128, 64, 4, 1>>(5),
+    make_variant<F16, ATTN_F16, Tile<128, 64, 4, 1>>(6),
+    make_variant<BF16, ATTN_BF16, Tile<64, 64, 8, 1>>(7),
+    make_variant<F16, ATTN_F16, Tile<64, 64, 8, 1>>(8),
+    make_variant<BF16, ATTN_BF16, Tile<128, 128, 4, 1>>(9),
+    make_variant<F16, ATTN_F16, Tile<128, 128, 4, 1>>(10),
+    make_variant<BF16, ATTN_BF16, Tile<128, 64, 4, 2>>(11),
+    make_variant<F16, ATTN_F16, Tile<128, 64, 4, 2>>(12),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -210,7 +219,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.xcd_remap = (plan.grid % 8 == 0 && plan.grid >= 8) ? 1 : 0;
   p.c = scale * kLog2e;
   p.thr = plan.thr;
-  hipError_t e = plan.var->launch(p, plan.grid, static_cast<hipStream_t>(stream));
+  hipError_t e = plan.var->launch(p, p.c < 0.0f, plan.grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, hipGetErrorString(e));
   return ATTN_OK;
 }
