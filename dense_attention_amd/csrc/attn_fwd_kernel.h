@@ -112,48 +112,98 @@ struct Tile {
   static constexpr int VS = D * 2 + 64;     // LDS row stride of V (bytes)
   static constexpr int K_TILE = BN * KS;
   static constexpr int V_TILE = BN * VS;
-  static constexpr int STAGE_BYTES = K_TILE + V_TILE;
-  static constexpr int STAGES = 2;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int STAGES = 2;           // two K and two V buffers
+  static constexpr int LDS_BYTES = STAGES * (K_TILE + V_TILE);
   // Waves per SIMD the register allocation targets.
   static constexpr int WPE = NW / 4;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile sizes");
   static_assert(K_TILE % 1024 == 0 && V_TILE % 1024 == 0, "tiles must be whole DMA blocks");
 };
 
-// One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4); the LDS
-// destination `dst` is wave-uniform and lane i writes dst + 16·i.  Kept as a
-// non-template function: the host compilation pass rejects the builtin inside
-// implicitly instantiated templates.
-__device__ __forceinline__ void dma16(const uint16_t* src, lds_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+// One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane i
+// reads base + voff and writes LDS address lds + 16·i; `base` and `lds` are
+// wave-uniform.  Written as inline assembly on purpose: the compiler then does
+// not track the copy as a pending LDS store, so it does not stall the next LDS
+// reads of *other* buffers on it.  Completion is awaited explicitly
+// (wait_vmem) before the workgroup barrier that publishes a tile, and no LDS
+// location is read while a copy into it is in flight.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, const lds_t* lds) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)lds;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(m0v)
+      : "memory", "m0");
 }
 
-// Issue the HBM -> LDS copy of rows kb .. kb+BN-1 of one head's K or V into a
-// padded tile of row stride STRIDE.  With LANE_ORDER, LDS row p of each
-// 32-row block receives key lane_key(p).  Rows past S are clamped to row S-1
-// (their scores are masked and their P is 0).  Pad slots are not loaded.
+// HBM -> LDS copy of one K or V tile (rows kb .. kb+BN-1 of one head) into a
+// padded LDS tile of row stride STRIDE.  Each wave owns BPW of the tile's
+// 1 KiB blocks; lane i of a block fills 16-byte slot i.  With LANE_ORDER, LDS
+// row p of each 32-row block receives key lane_key(p).  Pad slots are not
+// loaded.  The per-lane element offsets do not depend on the tile, so they are
+// computed once per kernel and a full tile costs one address add per block.
 template <class TL, int STRIDE, bool LANE_ORDER>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int kb, int S,
-                                         lds_t* dst, int wave, int lane) {
-  constexpr int SPR = STRIDE / 16;                  // 16-byte slots per LDS row
-  constexpr int BLOCKS = TL::BN * SPR / 64;         // 1 KiB blocks per tile
-  constexpr int BPW = (BLOCKS + TL::NW - 1) / TL::NW;
+struct DmaPlan {
+  static constexpr int SPR = STRIDE / 16;              // 16-byte slots per LDS row
+  static constexpr int BLOCKS = TL::BN * SPR / 64;     // 1 KiB blocks per tile
+  static constexpr int BPW = (BLOCKS + TL::NW - 1) / TL::NW;
+  // Byte offset of this lane's chunk from the tile's first row.  Pad slots load
+  // chunk 0 of their row again (the pad bytes of an LDS row are never read).
+  uint32_t off[BPW];
+
+  __device__ __forceinline__ static void slot_rc(int blk, int lane, int& key, int& c) {
+    const int slot = blk * 64 + lane;
+    const int p = slot / SPR;
+    c = slot - p * SPR;
+    if (c >= TL::DC) c = 0;
+    key = LANE_ORDER ? ((p & ~31) | lane_key(p & 31)) : p;
+  }
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int t = 0; t < BPW; ++t) {
-    const int blk = wave * BPW + t;
-    if (BLOCKS % TL::NW == 0 || blk < BLOCKS) {
-      const int slot = blk * 64 + lane;
-      const int p = slot / SPR;
-      const int c = slot - p * SPR;
-      if (c < TL::DC) {
-        const int key = LANE_ORDER ? ((p & ~31) | lane_key(p & 31)) : p;
-        const int grow = min(kb + key, S - 1);
-        dma16(src + (size_t)grow * TL::D + c * 8, dst + blk * 1024);
+    for (int t = 0; t < BPW; ++t) {
+      int key, c;
+      slot_rc(wave * BPW + t, lane, key, c);
+      off[t] = (uint32_t)(key * TL::D + c * 8) * 2u;
+    }
+  }
+
+  // Full tile starting at element `tile` (= head + kb·D).  `blk < BLOCKS` is
+  // wave-uniform.
+  __device__ __forceinline__ void issue(const uint16_t* tile, lds_t* dst, int wave) const {
+#pragma unroll
+    for (int t = 0; t < BPW; ++t) {
+      const int blk = wave * BPW + t;
+      if (BLOCKS % TL::NW == 0 || blk < BLOCKS) {
+        // Opaque per call: keeps the address as uniform base + 32-bit lane
+        // offset instead of a hoisted 64-bit per-lane pointer.
+        dma16(tile, off[t], dst + blk * 1024);
       }
     }
   }
-}
+
+  // Tile that may run past row S-1: such rows are clamped to row S-1 (their
+  // scores are masked and their P is 0).  The row is recovered from the offset
+  // (a row is 2·D bytes, a power of two).
+  __device__ __forceinline__ void issue_clamped(const uint16_t* head, int kb, int S, lds_t* dst,
+                                                int wave) const {
+    constexpr int ROW_BYTES = 2 * TL::D;
+    constexpr int ROW_SHIFT = ROW_BYTES == 256 ? 8 : 7;
+    static_assert(ROW_BYTES == (1 << ROW_SHIFT), "row size");
+#pragma unroll
+    for (int t = 0; t < BPW; ++t) {
+      const int blk = wave * BPW + t;
+      if (BLOCKS % TL::NW == 0 || blk < BLOCKS) {
+        const uint32_t o = off[t];
+        const int row = min(kb + (int)(o >> ROW_SHIFT), S - 1);
+        // Uniform base of row 0 plus a per-lane byte offset (rows < 2^23).
+        dma16(head, (uint32_t)row * ROW_BYTES + (o & (ROW_BYTES - 1)), dst + blk * 1024);
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ void wait_vmem() {
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
@@ -199,122 +249,237 @@ struct WaveState {
   float l[TL::QB];                       // lane-partial row sum relative to m
 };
 
-// One K/V tile: Sᵀ = K·Qᵀ, online softmax, Oᵀ += Vᵀ·Pᵀ.  MASK handles a
-// partial last tile (keys >= S get probability 0).  NEG is set when the score
-// multiplier c is negative: the largest c·s is then c·min(s).
-template <class T, class TL, bool MASK, bool NEG>
-__device__ __forceinline__ void tile_step(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
-                                          int kb, int S, float c, float thr, int lane) {
-  constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, NB = BN / 32, DB = D / 32, DT = D / 16;
-  const int lr = lane & 31;
-  const int hh = lane >> 5;
-  const lds_t* kbase_l = kl + lr * TL::KS + hh * 16;
+// ---- software-pipelined tile step --------------------------------------------
+//
+// The per-wave loop is software pipelined: while the softmax of tile j runs on
+// the VALU, the MFMA unit computes Sᵀ of tile j+1 and Oᵀ += Vᵀ·Pᵀ of tile j-1
+// (the steady state of "B200 Attention Kernel from Scratch to Near-SOTA in 60
+// Diagrams", Chapter 7 - Compute Pipeline, realised inside one wave's
+// instruction stream).  The three stages touch disjoint registers; the only
+// ordering constraint is that a rescale of O by tile j's alpha happens after
+// the P·V of tile j-1 and before that of tile j.
+//
+// One step is laid out as R regions separated by scheduling barriers.  Region
+// r issues QK MFMA r and PV MFMA r, the LDS reads of the operands two (K) and
+// one (V) regions ahead, and a slice of the softmax, so the MFMA unit and the
+// VALU work side by side while register pressure stays bounded.
 
-  // ---- Sᵀ = K · Qᵀ ----------------------------------------------------------
-  f32x16_t sacc[QB][NB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[qb][nb][i] = 0.f;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const u32x4_t a = ld_lds16(kbase_l + nb * 32 * TL::KS + t * 32);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb][nb] = Mma<T>::mfma(a, ws.qf[qb][t], sacc[qb][nb]);
-    }
-  }
+template <class TL>
+using SAcc = f32x16_t[TL::QB][TL::BN / 32];
+template <class TL>
+using PFrag = uint32_t[TL::QB][TL::BN / 32][8];
 
-  // ---- online softmax (base 2, lazy rescale) --------------------------------
-  const int kbase = kb + 16 * hh;  // key of accumulator entry 0 of block 0
-  constexpr float kInit = NEG ? __builtin_inff() : -__builtin_inff();
-  uint32_t pk[QB][NB][8];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float m4[4] = {kInit, kInit, kInit, kInit};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = sacc[qb][nb][i];
-        if (MASK && kbase + nb * 32 + i >= S) s = kInit;
-        m4[i & 3] = NEG ? fminf(m4[i & 3], s) : fmaxf(m4[i & 3], s);
-      }
-    float mx;
-    if (NEG)
-      mx = lane_pair_min(fminf(fminf(m4[0], m4[1]), fminf(m4[2], m4[3])));
-    else
-      mx = lane_pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-  const float mcand = mx * c;  // tile row maximum in log2 units
-    const float mold = ws.m[qb];
-    const bool rebase = (mold == -__builtin_inff()) || (mcand > mold + thr);
-    const float mnew = rebase ? mcand : mold;
-    if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(mold - mnew);  // 0 on the first tile
-      ws.l[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ws.o[qb][db][i] *= alpha;
-    }
-    ws.m[qb] = mnew;
-    const float nm = -mnew;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float pv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][nb][i], c, nm));
-        if (MASK && kbase + nb * 32 + i >= S) e = 0.f;
-        pv[i] = e;
-        ls[i & 3] += e;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pk[qb][nb][i] = Mma<T>::pack(pv[2 * i], pv[2 * i + 1]);
-    }
-    ws.l[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  }
+template <class T, class TL, bool QK, bool SM, bool MASK, bool NEG, bool PV>
+__device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
+                                          const SAcc<TL>& s_in, SAcc<TL>& s_out,
+                                          const PFrag<TL>& p_in, PFrag<TL>& p_out,
+                                          float (&alpha)[TL::QB], int kb, int S, float c,
+                                          float thr, int lane) {
+  constexpr int QB = TL::QB, NB = TL::BN / 32, DT = TL::D / 16, DB = TL::D / 32;
+  constexpr int NQ = NB * DT;        // K fragments (QK MFMA groups) per tile
+  constexpr int NP = NB * 2 * DB;    // V fragments (PV MFMA groups) per tile
+  constexpr int R = NQ > NP ? NQ : NP;
+  constexpr int NV = NB * 16;        // scores per lane per 32-query block
+  constexpr int NPAIR = QB * NV / 2; // packed P words per lane
+  static_assert(R >= 3, "pipeline needs at least three regions");
 
-  // ---- Oᵀ += Vᵀ · Pᵀ ----------------------------------------------------------
-  // Transpose-read geometry: lane group g = lane/16 covers key half h = g/2 and
-  // head-dim half gp = g%2; inside the group, lane i reads key row i/4 and the
-  // 8-byte piece of head-dim columns chosen so that the result is lane_key-ordered.
+  // Per-lane LDS bases.  K rows are in MFMA-lane order; the V transpose read:
+  // lane group g = lane/16 covers key half g/2 and head-dim half g%2; inside
+  // the group, lane i reads key row i/4 and the 8-byte piece of head-dim
+  // columns chosen so that the result is lane_key-ordered.
+  const lds_t* kbase = kl + (lane & 31) * TL::KS + (lane >> 5) * 16;
   const int g = lane >> 4;
   const int li = lane & 15;
-  const lds_t* vbase_l = vl + (16 * (g >> 1) + (li >> 2)) * TL::VS +
-                         (2 * (li & 1) + (g & 1)) * 16 + ((li >> 1) & 1) * 8;
+  const lds_t* vbase = vl + (16 * (g >> 1) + (li >> 2)) * TL::VS +
+                       (2 * (li & 1) + (g & 1)) * 16 + ((li >> 1) & 1) * 8;
+
+  auto kfrag = [&](int i) -> u32x4_t {
+    return ld_lds16(kbase + (i / DT) * 32 * TL::KS + (i % DT) * 32);
+  };
+  auto vfrag = [&](int i) -> u32x4_t {
+    const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
+    const lds_t* pv0 = vbase + (nb * 32 + 8 * mm) * TL::VS + db * 64;
+    const u32x2_t lo = ld_lds_tr(pv0);
+    const u32x2_t hi = ld_lds_tr(pv0 + 4 * TL::VS);
+    const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+    return a;
+  };
+
+  u32x4_t kf[NQ];
+  u32x4_t vf[NP];
+  if (QK) {
+    kf[0] = kfrag(0);
+    kf[1] = kfrag(1);
+  }
+  if (PV) vf[0] = vfrag(0);
+
+  // softmax state.  Key kb + 16·hh + 32·nb + i of a tile is valid iff
+  // 32·nb + i < lim; lim is opaque so the compares stay inside the step.
+  int lim = S - (kb + 16 * (lane >> 5));
+  if (MASK) asm volatile("" : "+v"(lim));
+  constexpr float kInit = NEG ? __builtin_inff() : -__builtin_inff();
+  float mx[QB], nm[QB], ls[QB][2];
+  bool any = false;
+  const f32x16_t zero = {};
+
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int r = 0; r < R; ++r) {
+    // ---- MFMA work of region r ----
+    if (QK && r < NQ) {
+      const int nb = r / DT, t = r % DT;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
+      for (int qb = 0; qb < QB; ++qb)
+        s_out[qb][nb] = Mma<T>::mfma(kf[r], ws.qf[qb][t], t == 0 ? zero : s_out[qb][nb]);
+      if (r + 2 < NQ) kf[r + 2] = kfrag(r + 2);
+    }
+    if (PV && r < NP) {
+      const int nb = r / (2 * DB), mm = (r / DB) % 2, db = r % DB;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const lds_t* pv0 = vbase_l + (nb * 32 + 8 * mm) * TL::VS + db * 64;
-        const u32x2_t lo = ld_lds_tr(pv0);
-        const u32x2_t hi = ld_lds_tr(pv0 + 4 * TL::VS);
-        const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+      for (int qb = 0; qb < QB; ++qb) {
+        const u32x4_t b = {p_in[qb][nb][4 * mm + 0], p_in[qb][nb][4 * mm + 1],
+                           p_in[qb][nb][4 * mm + 2], p_in[qb][nb][4 * mm + 3]};
+        ws.o[qb][db] = Mma<T>::mfma(vf[r], b, ws.o[qb][db]);
+      }
+      if (r + 1 < NP) vf[r + 1] = vfrag(r + 1);
+    }
+    // ---- softmax slice of region r ----
+    if (SM) {
+      if (r == 0) {
+        // Row maximum of the tile (4 independent chains per lane).
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const u32x4_t b = {pk[qb][nb][4 * mm + 0], pk[qb][nb][4 * mm + 1],
-                             pk[qb][nb][4 * mm + 2], pk[qb][nb][4 * mm + 3]};
-          ws.o[qb][db] = Mma<T>::mfma(a, b, ws.o[qb][db]);
+          float m4[4] = {kInit, kInit, kInit, kInit};
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            float x = s_in[qb][v / 16][v % 16];
+            if (MASK && (v / 16) * 32 + (v % 16) >= lim) x = kInit;
+            m4[v & 3] = NEG ? fminf(m4[v & 3], x) : fmaxf(m4[v & 3], x);
+          }
+          mx[qb] = NEG ? fminf(fminf(m4[0], m4[1]), fminf(m4[2], m4[3]))
+                       : fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        }
+      } else if (r == 1) {
+        // Exchange with the other lane half, threshold-guarded move of m.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float tm = NEG ? lane_pair_min(mx[qb]) : lane_pair_max(mx[qb]);
+          const float mcand = tm * c;  // tile row maximum in log2 units
+          const float mold = ws.m[qb];
+          const bool rebase = (mold == -__builtin_inff()) || (mcand > mold + thr);
+          const float mnew = rebase ? mcand : mold;
+          alpha[qb] = __builtin_amdgcn_exp2f(mold - mnew);  // 1 if kept, 0 on the first tile
+          any = any || (__builtin_amdgcn_ballot_w64(rebase) != 0);
+          ws.m[qb] = mnew;
+          nm[qb] = -mnew;
+          ls[qb][0] = 0.f;
+          ls[qb][1] = 0.f;
+        }
+      } else {
+        // p = 2^(s·c - m), row-sum partials in fp32, P rounded and packed.
+#pragma unroll
+        for (int k = 0; k < NPAIR; ++k) {
+          if (2 + (k * (R - 2)) / NPAIR != r) continue;
+          const int qb = k / (NV / 2), w = k % (NV / 2), nb = w / 8, i = 2 * (w % 8);
+          float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[qb][nb][i], c, nm[qb]));
+          float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[qb][nb][i + 1], c, nm[qb]));
+          if (MASK && nb * 32 + i >= lim) e0 = 0.f;
+          if (MASK && nb * 32 + i + 1 >= lim) e1 = 0.f;
+          ls[qb][0] += e0;
+          ls[qb][1] += e1;
+          uint32_t pw = Mma<T>::pack(e0, e1);
+          asm volatile("" : "+v"(pw));  // keep the packing here, not sunk to the step's end
+          p_out[qb][nb][i / 2] = pw;
+        }
+        if (r == R - 1) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) ws.l[qb] = ws.l[qb] * alpha[qb] + (ls[qb][0] + ls[qb][1]);
         }
       }
     }
+    if ((QK ? 1 : 0) + (SM ? 1 : 0) + (PV ? 1 : 0) > 1) __builtin_amdgcn_sched_barrier(0);
   }
+  return any;
+}
+
+template <class TL>
+__device__ __forceinline__ void rescale_o(WaveState<TL>& ws, const float (&alpha)[TL::QB]) {
+#pragma unroll
+  for (int qb = 0; qb < TL::QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < TL::D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ws.o[qb][db][i] *= alpha[qb];
+}
+
+// LDS ring: two K buffers then two V buffers; K_t lives in K buffer t%2 and V_t
+// in V buffer t%2.
+template <class TL>
+struct Ring {
+  lds_t* base;
+  __device__ __forceinline__ lds_t* k(int t) const { return base + (t & 1) * TL::K_TILE; }
+  __device__ __forceinline__ lds_t* v(int t) const {
+    return base + 2 * TL::K_TILE + (t & 1) * TL::V_TILE;
+  }
+};
+
+template <class TL>
+struct Copies {
+  DmaPlan<TL, TL::KS, true> k;
+  DmaPlan<TL, TL::VS, false> v;
+};
+
+// ---- ping-pong schedule ------------------------------------------------------
+//
+// Every wave runs the same sequence of phases, separated by workgroup
+// barriers:  M(i) = P·V of tile i-1 then Sᵀ of tile i (MFMA),  V(i) = softmax
+// of tile i (VALU).  With 8 waves, waves w and w+4 share a SIMD; group 1
+// (waves 4-7) starts one barrier later than group 0, so on every SIMD one wave
+// keeps the MFMA unit busy while the other keeps the VALU busy:
+//     slot 2i:   group 0 M(i)     group 1 V(i-1)
+//     slot 2i+1: group 0 V(i)     group 1 M(i)
+// (the producer/consumer overlap that the warp-specialised kernels of "B200
+// Attention Kernel from Scratch to Near-SOTA in 60 Diagrams", Chapter 4 - Warp
+// Specialization, and "Attention for sm90, Line by Line", "Why does a flash
+// attention kernel need three warpgroups?", obtain with separate roles).
+// Copies: in slot 2i every wave issues its share of K_{i+1} and V_i, and
+// waits for them at the end of slot 2i+1.  K_i is read in slots 2i and 2i+1
+// and V_{i-1} in the same two slots, so a buffer refilled in slot 2i+2 (two
+// tiles later) is no longer read.
+
+template <class T, class TL, bool QK, bool PV, bool NEG>
+__device__ __forceinline__ void mfma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
+                                           SAcc<TL>& sacc, PFrag<TL>& pfr, int lane) {
+  float alpha[TL::QB];
+  __builtin_amdgcn_s_setprio(1);
+  pipe_step<T, TL, QK, false, false, NEG, PV>(ws, kl, vl, sacc, sacc, pfr, pfr, alpha, 0, 0, 0.f,
+                                              0.f, lane);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+template <class T, class TL, bool MASK, bool NEG>
+__device__ __forceinline__ void valu_phase(WaveState<TL>& ws, int i, int S, float c, float thr,
+                                           SAcc<TL>& sacc, PFrag<TL>& pfr, int lane) {
+  float alpha[TL::QB];
+  const bool any = pipe_step<T, TL, false, true, MASK, NEG, false>(
+      ws, nullptr, nullptr, sacc, sacc, pfr, pfr, alpha, i * TL::BN, S, c, thr, lane);
+  // O has received P·V of tile i-1 and not yet that of tile i.
+  if (any) rescale_o(ws, alpha);
 }
 
 template <class T, class TL, bool NEG>
-__device__ __forceinline__ void process_item(const Params& p, lds_t* smem, int item, int wave,
-                                             int lane) {
+__device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& cp, lds_t* smem,
+                                             int item, int wave, int lane) {
   constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, DB = D / 32, DT = D / 16;
   const int lr = lane & 31;
   const int hh = lane >> 5;
-  const int S = p.S;
+  // S passes through an empty asm so that per-lane values derived from it
+  // (tail masks, clamped copy addresses) are recomputed per item instead of
+  // being hoisted out of the persistent loop, where they would occupy
+  // registers for the whole kernel.
+  int S = p.S;
+  asm volatile("" : "+s"(S));
+  const float c = p.c, thr = p.thr;
+  const int grp = TL::NW == 8 ? (wave >> 2) : 0;
 
   const int bh = item / p.n_qtiles;
   const int qt = item - bh * p.n_qtiles;
@@ -322,13 +487,31 @@ __device__ __forceinline__ void process_item(const Params& p, lds_t* smem, int i
   const uint16_t* __restrict__ qh = p.q + head;
   const uint16_t* __restrict__ kh = p.k + head;
   const uint16_t* __restrict__ vh = p.v + head;
-
   const int nt = (S + BN - 1) / BN;
+  const bool ragged = (S % BN) != 0;
+  const Ring<TL> ring{smem};
 
-  // Start the first K/V tile, then load Q while it flies.
-  dma_tile<TL, TL::KS, true>(kh, 0, S, smem, wave, lane);
-  dma_tile<TL, TL::VS, false>(vh, 0, S, smem + TL::K_TILE, wave, lane);
+  // Copies of slot 2i: K_{i+1} and V_i.
+  auto copies = [&](int i) {
+    if (i + 1 < nt) {
+      if ((i + 2) * BN <= S)
+        cp.k.issue(kh + (size_t)(i + 1) * BN * D, ring.k(i + 1), wave);
+      else
+        cp.k.issue_clamped(kh, (i + 1) * BN, S, ring.k(i + 1), wave);
+    }
+    if (i < nt) {
+      if ((i + 1) * BN <= S)
+        cp.v.issue(vh + (size_t)i * BN * D, ring.v(i), wave);
+      else
+        cp.v.issue_clamped(vh, i * BN, S, ring.v(i), wave);
+    }
+  };
 
+  // Prologue: K_0 in flight while Q is loaded into registers.
+  if (BN <= S)
+    cp.k.issue(kh, ring.k(0), wave);
+  else
+    cp.k.issue_clamped(kh, 0, S, ring.k(0), wave);
   WaveState<TL> ws;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -349,26 +532,67 @@ __device__ __forceinline__ void process_item(const Params& p, lds_t* smem, int i
   wait_vmem();
   __syncthreads();
 
-  // Full tiles.  The copy of tile j+1 is issued before tile j is computed and
-  // waited for after it.
-  const int nfull = S / BN;
-  for (int j = 0; j < nfull; ++j) {
-    const lds_t* kl = smem + (j & 1) * TL::STAGE_BYTES;
-    if (j + 1 < nt) {
-      lds_t* nk = smem + ((j + 1) & 1) * TL::STAGE_BYTES;
-      dma_tile<TL, TL::KS, true>(kh, (j + 1) * BN, S, nk, wave, lane);
-      dma_tile<TL, TL::VS, false>(vh, (j + 1) * BN, S, nk + TL::K_TILE, wave, lane);
+  SAcc<TL> sacc;
+  PFrag<TL> pfr;
+  if (grp == 1) {  // group 1 sits out slot 0
+    copies(0);
+    __syncthreads();
+  }
+  // Step 0: Sᵀ of tile 0, softmax of tile 0.
+  if (grp == 0) copies(0);
+  mfma_phase<T, TL, true, false, NEG>(ws, ring.k(0), nullptr, sacc, pfr, lane);
+  if (grp == 1) wait_vmem();
+  __syncthreads();
+  if (grp == 1 && nt > 1) copies(1);
+  if (nt == 1 && ragged)
+    valu_phase<T, TL, true, NEG>(ws, 0, S, c, thr, sacc, pfr, lane);
+  else
+    valu_phase<T, TL, false, NEG>(ws, 0, S, c, thr, sacc, pfr, lane);
+  if (grp == 0) wait_vmem();
+  __syncthreads();
+  // Steps 1 .. nt-1: P·V of tile i-1 and Sᵀ of tile i, softmax of tile i.
+  // Steps 1 .. nt-3 copy only whole tiles and softmax unmasked tiles; the last
+  // two steps are peeled so the steady loop carries no such branches.
+  auto step = [&](int i) {
+    if (grp == 0) copies(i);
+    mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
+    if (grp == 1) wait_vmem();
+    __syncthreads();
+    if (grp == 1) copies(i + 1);
+    if (i == nt - 1 && ragged)
+      valu_phase<T, TL, true, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
+    else
+      valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
+    if (grp == 0) wait_vmem();
+    __syncthreads();
+  };
+  for (int i = 1; i <= nt - 3; ++i) {
+    if (grp == 0) {
+      cp.k.issue(kh + (size_t)(i + 1) * BN * D, ring.k(i + 1), wave);
+      cp.v.issue(vh + (size_t)i * BN * D, ring.v(i), wave);
     }
-    tile_step<T, TL, false, NEG>(ws, kl, kl + TL::K_TILE, j * BN, S, p.c, p.thr, lane);
-    wait_vmem();
+    mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
+    if (grp == 1) wait_vmem();
+    __syncthreads();
+    if (grp == 1) {
+      if (i + 2 < nt) {
+        if ((i + 3) * BN <= S)
+          cp.k.issue(kh + (size_t)(i + 2) * BN * D, ring.k(i + 2), wave);
+        else
+          cp.k.issue_clamped(kh, (i + 2) * BN, S, ring.k(i + 2), wave);
+      }
+      cp.v.issue(vh + (size_t)(i + 1) * BN * D, ring.v(i + 1), wave);
+    }
+    valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
+    if (grp == 0) wait_vmem();
     __syncthreads();
   }
-  // Partial last tile (S not a multiple of BN), with keys >= S masked.
-  if (nfull < nt) {
-    const lds_t* kl = smem + (nfull & 1) * TL::STAGE_BYTES;
-    tile_step<T, TL, true, NEG>(ws, kl, kl + TL::K_TILE, nfull * BN, S, p.c, p.thr, lane);
-    __syncthreads();
-  }
+  if (nt >= 3) step(nt - 2);
+  if (nt >= 2) step(nt - 1);
+  // Step nt: P·V of the last tile.
+  mfma_phase<T, TL, false, true, NEG>(ws, nullptr, ring.v(nt - 1), sacc, pfr, lane);
+  if (grp == 0) __syncthreads();  // group 1 has one barrier fewer to go
+  __syncthreads();
 
   // ---- epilogue: O / l, round, store; LSE ------------------------------------
 #pragma unroll
@@ -405,6 +629,9 @@ void attn_fwd_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int G = gridDim.x;
+  Copies<TL> cp;
+  cp.k.init(wave, lane);
+  cp.v.init(wave, lane);
   // Persistent loop over work items ("B200 Attention Kernel from Scratch to
   // Near-SOTA in 60 Diagrams", Chapter 14 - Persistent: a static grid-stride
   // assignment).  Workgroups are dispatched round-robin over the 8 XCDs, so
@@ -416,7 +643,7 @@ void attn_fwd_kernel(Params p) {
     if (base >= p.n_items) break;
     int item = base + (int)blockIdx.x;
     if (p.xcd_remap) item = base + (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
-    if (item < p.n_items) process_item<T, TL, NEG>(p, smem, item, wave, lane);
+    if (item < p.n_items) process_item<T, TL, NEG>(p, cp, smem, item, wave, lane);
   }
 }
 
