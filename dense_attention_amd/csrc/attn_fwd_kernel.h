@@ -249,20 +249,18 @@ struct WaveState {
   float l[TL::QB];                       // lane-partial row sum relative to m
 };
 
-// ---- software-pipelined tile step --------------------------------------------
+// ---- work of one tile step ------------------------------------------------------
 //
-// The per-wave loop is software pipelined: while the softmax of tile j runs on
-// the VALU, the MFMA unit computes Sᵀ of tile j+1 and Oᵀ += Vᵀ·Pᵀ of tile j-1
-// (the steady state of "B200 Attention Kernel from Scratch to Near-SOTA in 60
-// Diagrams", Chapter 7 - Compute Pipeline, realised inside one wave's
-// instruction stream).  The three stages touch disjoint registers; the only
-// ordering constraint is that a rescale of O by tile j's alpha happens after
-// the P·V of tile j-1 and before that of tile j.
-//
-// One step is laid out as R regions separated by scheduling barriers.  Region
-// r issues QK MFMA r and PV MFMA r, the LDS reads of the operands two (K) and
-// one (V) regions ahead, and a slice of the softmax, so the MFMA unit and the
-// VALU work side by side while register pressure stays bounded.
+// pipe_step performs any combination of the three stages of a K/V tile:
+//   QK: Sᵀ = K·Qᵀ for the tile in `kl`,
+//   SM: online softmax of the scores in `s_in` (writes P to `p_out`),
+//   PV: Oᵀ += Vᵀ·Pᵀ with the tile in `vl` and P from `p_in`.
+// The stages touch disjoint registers.  The work is laid out as R regions:
+// region r issues QK MFMA r and PV MFMA r together with the LDS reads of
+// their operands two (K) and one (V) regions ahead, so every MFMA finds its
+// operands loaded.  When the softmax runs alone it is issued as wide
+// independent passes (see below); when it runs beside MFMAs its slices are
+// spread over the regions and scheduling barriers keep them there.
 
 template <class TL>
 using SAcc = f32x16_t[TL::QB][TL::BN / 32];
@@ -376,6 +374,39 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
         }
       } else {
         // p = 2^(s·c - m), row-sum partials in fp32, P rounded and packed.
+        if (!QK && !PV) {
+          // Softmax-only phase: a single wave of the SIMD issues it, so expose
+          // the most independent work: all FMAs, then all exp2, then the sums
+          // and the packing.
+          if (r == 2) {
+            float e[QB][NV];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+              for (int v = 0; v < NV; ++v)
+                e[qb][v] = __builtin_fmaf(s_in[qb][v / 16][v % 16], c, nm[qb]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+              for (int v = 0; v < NV; ++v) e[qb][v] = __builtin_amdgcn_exp2f(e[qb][v]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int v = 0; v < NV; ++v) {
+                if (MASK && (v / 16) * 32 + (v % 16) >= lim) e[qb][v] = 0.f;
+                l4[v & 3] += e[qb][v];
+              }
+              ls[qb][0] = l4[0] + l4[1];
+              ls[qb][1] = l4[2] + l4[3];
+#pragma unroll
+              for (int w = 0; w < NV / 2; ++w)
+                p_out[qb][w / 8][w % 8] = Mma<T>::pack(e[qb][2 * w], e[qb][2 * w + 1]);
+            }
+          }
+        } else {
 #pragma unroll
         for (int k = 0; k < NPAIR; ++k) {
           if (2 + (k * (R - 2)) / NPAIR != r) continue;
@@ -389,6 +420,7 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
           uint32_t pw = Mma<T>::pack(e0, e1);
           asm volatile("" : "+v"(pw));  // keep the packing here, not sunk to the step's end
           p_out[qb][nb][i / 2] = pw;
+        }
         }
         if (r == R - 1) {
 #pragma unroll
@@ -428,6 +460,41 @@ struct Copies {
   DmaPlan<TL, TL::VS, false> v;
 };
 
+// Epilogue of a work item: O / l rounded to the output type, and the LSE.
+template <class T, class TL>
+__device__ __forceinline__ void store_output(const Params& p, const WaveState<TL>& ws, size_t head,
+                                             int bh, int qt, int wave, int lane) {
+  constexpr int D = TL::D, QB = TL::QB, DB = D / 32;
+  const int lr = lane & 31;
+  const int hh = lane >> 5;
+  const int S = p.S;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = lane_pair_sum(ws.l[qb]);
+    const int row = qt * TL::BM + (wave * QB + qb) * 32 + lr;
+    if (row < S) {
+      const float inv = 1.0f / lt;
+      uint16_t* orow = p.o + head + (size_t)row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          w[i] = Mma<T>::pack(ws.o[qb][db][2 * i] * inv, ws.o[qb][db][2 * i + 1] * inv);
+        u32x4_t w0 = {w[0], w[1], w[2], w[3]};
+        u32x4_t w1 = {w[4], w[5], w[6], w[7]};
+        *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh) = w0;
+        *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh + 8) = w1;
+      }
+      if (p.lse != nullptr && hh == 0) {
+        // ln(sum_j exp(s_j * scale)) = (m + log2(l)) * ln 2
+        p.lse[(size_t)bh * S + row] = (ws.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
+      }
+    }
+  }
+}
+
+
 // ---- ping-pong schedule ------------------------------------------------------
 //
 // Every wave runs the same sequence of phases, separated by workgroup
@@ -450,10 +517,8 @@ template <class T, class TL, bool QK, bool PV, bool NEG>
 __device__ __forceinline__ void mfma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
                                            SAcc<TL>& sacc, PFrag<TL>& pfr, int lane) {
   float alpha[TL::QB];
-  __builtin_amdgcn_s_setprio(1);
   pipe_step<T, TL, QK, false, false, NEG, PV>(ws, kl, vl, sacc, sacc, pfr, pfr, alpha, 0, 0, 0.f,
                                               0.f, lane);
-  __builtin_amdgcn_s_setprio(0);
 }
 
 template <class T, class TL, bool MASK, bool NEG>
@@ -594,32 +659,9 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   if (grp == 0) __syncthreads();  // group 1 has one barrier fewer to go
   __syncthreads();
 
-  // ---- epilogue: O / l, round, store; LSE ------------------------------------
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = lane_pair_sum(ws.l[qb]);
-    const int row = qt * TL::BM + (wave * QB + qb) * 32 + lr;
-    if (row < S) {
-      const float inv = 1.0f / lt;
-      uint16_t* orow = p.o + head + (size_t)row * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          w[i] = Mma<T>::pack(ws.o[qb][db][2 * i] * inv, ws.o[qb][db][2 * i + 1] * inv);
-        u32x4_t w0 = {w[0], w[1], w[2], w[3]};
-        u32x4_t w1 = {w[4], w[5], w[6], w[7]};
-        *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh) = w0;
-        *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh + 8) = w1;
-      }
-      if (p.lse != nullptr && hh == 0) {
-        // ln(sum_j exp(s_j * scale)) = (m + log2(l)) * ln 2
-        p.lse[(size_t)bh * S + row] = (ws.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
-      }
-    }
-  }
+  store_output<T, TL>(p, ws, head, bh, qt, wave, lane);
 }
+
 
 template <class T, class TL, bool NEG>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
