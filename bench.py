@@ -56,21 +56,34 @@ def measured_traffic(workload: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, rows: int):
-    """Times the float64 oracle on `rows` whole query rows of head (0, 0)."""
-    import numpy as np
+def cpu_baseline(w, q, k, v, seconds: float):
+    """Times the float64 oracle on whole heads of the workload for about `seconds`.
+
+    Heads (b, h) are taken in order until the time budget is spent (at least
+    one head); every query row of a sampled head is computed against all of
+    its keys, exactly as for the full workload.
+    """
     import threadpoolctl
     import workloads as W
-    from oracle import attention_rows
+    from oracle import attention_forward
 
-    qn = W.to_f64(q[:1, :1])
-    kn = W.to_f64(k[:1, :1])
-    vn = W.to_f64(v[:1, :1])
-    sel = np.arange(rows)
+    flops = 0.0
+    heads = 0
     t0 = time.perf_counter()
-    attention_rows(qn, kn, vn, w.scale, 0, 0, sel)
+    for b in range(w.B):
+        for h in range(w.H):
+            qn = W.to_f64(q[b:b + 1, h:h + 1])
+            kn = W.to_f64(k[b:b + 1, h:h + 1])
+            vn = W.to_f64(v[b:b + 1, h:h + 1])
+            attention_forward(qn, kn, vn, w.scale)
+            flops += 4.0 * w.S * w.S * w.D
+            heads += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        else:
+            continue
+        break
     dt = time.perf_counter() - t0
-    flops = 4.0 * rows * w.S * w.D
     blas = [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
             if p.get("user_api") == "blas"]
     cores = max(blas) if blas else 1
@@ -79,9 +92,9 @@ def cpu_baseline(w, q, k, v, rows: int):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"{rows} query rows x {w.S} keys of head (0,0), D={w.D}, float64 numpy "
-                   f"(BLAS matmul on {cores} threads, exp single-threaded); {dt:.1f} s on "
-                   f"{os.cpu_count()} visible CPUs"),
+        "sample": (f"{heads} of {w.B * w.H} heads, all {w.S} query rows each against all keys, "
+                   f"D={w.D}, float64 numpy (BLAS matmul on {cores} threads, exp single-threaded); "
+                   f"{dt:.1f} s on {os.cpu_count()} visible CPUs"),
     }
 
 
@@ -112,9 +125,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-rows", type=int, default=4096,
-                    help="query rows of the oracle's CPU-baseline sample (0 skips it)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the oracle's CPU-baseline sample (0 skips it)")
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed back-to-back launches before the warmup steps, so GPU clocks "
+                         "reach their loaded steady state (0 disables)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(calibrates the HBM byte counters of rocprofv3)")
@@ -144,6 +160,12 @@ def main():
     def step():
         da.attn_fwd_ex(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant)
 
+    # Clock settle (untimed): the first ~100 ms of load run at transitional clocks.
+    t_settle = time.perf_counter()
+    while args.settle_ms > 0 and (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -190,8 +212,8 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if args.cpu_rows > 0:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(args.cpu_rows, w.S))
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
