@@ -45,7 +45,7 @@ def _as_f64(x) -> np.ndarray:
 
 
 def _rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float):
-    """Attention of the query rows ``qh`` [R, D] against one head's keys/values [S, D]."""
+    """Attention of the query rows ``qh`` [R, D] against one head's keys/values [Skv, D]."""
     s = scale * (qh @ kh.T)                 # [R, S] scores
     m = s.max(axis=1, keepdims=True)        # [R, 1] row maxima
     e = np.exp(s - m)                       # [R, S]
@@ -56,11 +56,14 @@ def _rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float):
 
 
 def attention_forward(q, k, v, scale: float, row_block: int = 1024):
-    """Full forward over [B, H, S, D] inputs.  Returns (o [B,H,S,D], lse [B,H,S]) in float64."""
+    """Full forward.  q is [B, H, Sq, D]; k and v are [B, H, Skv, D] (Skv >= 1; the
+    usual self-attention case has Skv = Sq).  Every query row attends to all Skv
+    keys of its head.  Returns (o [B,H,Sq,D], lse [B,H,Sq]) in float64."""
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, H, S, D = q.shape
-    if k.shape != (B, H, S, D) or v.shape != (B, H, S, D):
-        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    Skv = k.shape[2]
+    if k.shape != (B, H, Skv, D) or v.shape != (B, H, Skv, D) or Skv < 1:
+        raise ValueError("k and v must be [B, H, Skv, D] with Skv >= 1 and q's B, H, D")
     o = np.empty((B, H, S, D), dtype=np.float64)
     lse = np.empty((B, H, S), dtype=np.float64)
     for b in range(B):

@@ -63,15 +63,16 @@ def pin_golden_fractions(fwd):
 def _brute(q, k, v, scale):
     """Independent arrangement: weight of key t for query i is 1 / sum_j exp(s_ij - s_it)."""
     B, H, S, D = q.shape
+    Skv = k.shape[2]
     o = np.zeros((B, H, S, D))
     lse = np.zeros((B, H, S))
     for b in range(B):
         for h in range(H):
             for i in range(S):
                 s = [scale * math.fsum(q[b, h, i, d] * k[b, h, j, d] for d in range(D))
-                     for j in range(S)]
-                for t in range(S):
-                    w = 1.0 / math.fsum(math.exp(s[j] - s[t]) for j in range(S))
+                     for j in range(Skv)]
+                for t in range(Skv):
+                    w = 1.0 / math.fsum(math.exp(s[j] - s[t]) for j in range(Skv))
                     for d in range(D):
                         o[b, h, i, d] += w * v[b, h, t, d]
                 lse[b, h, i] = math.log(math.fsum(math.exp(x) for x in s))
@@ -89,6 +90,15 @@ def pin_brute_force_tiny(fwd):
         bo, bl = _brute(q, k, v, scale)
         np.testing.assert_allclose(np.asarray(o), bo, rtol=0, atol=1e-12)
         np.testing.assert_allclose(np.asarray(lse), bl, rtol=0, atol=1e-12)
+    # queries and keys of different lengths (a key subset, or cross attention)
+    for (B, H, Sq, Skv, D, scale) in [(1, 1, 2, 5, 3, 0.8), (2, 1, 6, 1, 2, 1.0), (1, 2, 3, 8, 4, 0.5)]:
+        q = rng.integers(-3, 4, size=(B, H, Sq, D)).astype(np.float64)
+        k = rng.integers(-3, 4, size=(B, H, Skv, D)).astype(np.float64)
+        v = rng.normal(size=(B, H, Skv, D))
+        o, lse = fwd(q, k, v, scale)
+        bo, bl = _brute(q, k, v, scale)
+        np.testing.assert_allclose(np.asarray(o), bo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(np.asarray(lse), bl, rtol=0, atol=1e-12)
 
 
 def pin_torch_sdpa(fwd):
@@ -97,10 +107,11 @@ def pin_torch_sdpa(fwd):
     from scipy.special import logsumexp
 
     rng = _rng(99)
-    for (B, H, S, D) in [(1, 4, 128, 64), (1, 2, 512, 64), (2, 2, 100, 128), (1, 1, 33, 16)]:
+    for (B, H, S, Skv, D) in [(1, 4, 128, 128, 64), (1, 2, 512, 512, 64), (2, 2, 100, 100, 128),
+                              (1, 1, 33, 33, 16), (1, 2, 37, 211, 64), (2, 1, 300, 7, 128)]:
         q = rng.standard_normal((B, H, S, D))
-        k = rng.standard_normal((B, H, S, D))
-        v = rng.standard_normal((B, H, S, D))
+        k = rng.standard_normal((B, H, Skv, D))
+        v = rng.standard_normal((B, H, Skv, D))
         scale = 1.0 / math.sqrt(D)
         o, lse = fwd(q, k, v, scale)
         ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),

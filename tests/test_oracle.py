@@ -39,8 +39,12 @@ def test_row_blocking_does_not_change_result():
 
 
 def test_rejects_mismatched_shapes():
-    with pytest.raises(ValueError):
-        attention_forward(np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 5, 2)), np.zeros((1, 1, 5, 2)), 1.0)
+    with pytest.raises(ValueError):   # k and v lengths differ
+        attention_forward(np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 5, 2)), np.zeros((1, 1, 6, 2)), 1.0)
+    with pytest.raises(ValueError):   # head dimension differs
+        attention_forward(np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 5, 3)), np.zeros((1, 1, 5, 3)), 1.0)
+    with pytest.raises(ValueError):   # no keys
+        attention_forward(np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 0, 2)), np.zeros((1, 1, 0, 2)), 1.0)
 
 
 # --- planted mistakes -------------------------------------------------------
