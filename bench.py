@@ -128,6 +128,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle's CPU-baseline sample (0 skips it)")
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--kv-splits", type=int, default=-1,
+                    help="-1: attn_fwd; 0: attn_fwd_split with the library's split count; "
+                         "n > 0: attn_fwd_split with at most n key ranges (partials + merge)")
+    ap.add_argument("--layout", choices=["bhsd", "bshd"], default="bhsd",
+                    help="bshd: inputs and output stored token-major [B, S, H, D], run through "
+                         "attn_fwd_strided without conversion copies")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed back-to-back launches before the warmup steps, so GPU clocks "
                          "reach their loaded steady state (0 disables)")
@@ -152,13 +158,29 @@ def main():
     q, k, v = W.workload_qkv(w)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    od = torch.empty_like(qd)
+    if args.layout == "bshd":
+        qd, kd, vd = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2) for t in (q, k, v))
+        od = torch.empty((w.B, w.S, w.H, w.D), dtype=q.dtype, device=dev).transpose(1, 2)
+    else:
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        od = torch.empty_like(qd)
     lsed = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.kv_splits >= 0 and args.layout != "bhsd":
+        sys.exit("bench.py: --kv-splits runs on the contiguous [B, H, S, D] layout only")
+    ws = None
+    if args.kv_splits >= 0:
+        nbytes = da.attn_fwd_split_workspace_size(w.B, w.H, w.S, w.D, args.kv_splits)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
 
     def step():
-        da.attn_fwd_ex(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant)
+        if args.kv_splits >= 0:
+            da.attn_fwd_split(qd, kd, vd, od, lsed, w.scale, kv_splits=args.kv_splits,
+                              workspace=ws, stream=stream, variant=args.variant)
+        elif args.layout == "bshd":
+            da.attn_fwd_strided(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant)
+        else:
+            da.attn_fwd_ex(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant)
 
     # Clock settle (untimed): the first ~100 ms of load run at transitional clocks.
     t_settle = time.perf_counter()
@@ -200,7 +222,10 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: iid N(0,1) q/k/v from numpy PCG64 seed, rounded to dtype",
-        "config": dict(w.as_dict(), kernel=cfg),
+        "config": dict(w.as_dict(), kernel=cfg, api=("attn_fwd" if args.kv_splits < 0 and args.layout == "bhsd"
+                                                     else "attn_fwd_strided" if args.kv_splits < 0
+                                                     else f"attn_fwd_split(kv_splits={args.kv_splits})"),
+                       layout=args.layout),
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {
             "bound": "mfma",

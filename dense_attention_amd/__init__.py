@@ -14,12 +14,15 @@ import os
 import threading
 
 __all__ = [
-    "ATTN_F16", "ATTN_BF16", "AttnError", "attn_fwd", "attn_fwd_ex", "attn_get_config",
-    "attn_variants", "attn_strerror", "library_path", "load_library",
+    "ATTN_F16", "ATTN_BF16", "ATTN_F32", "AttnError", "attn_fwd", "attn_fwd_ex",
+    "attn_fwd_strided", "attn_fwd_partial", "attn_merge", "attn_fwd_split",
+    "attn_fwd_split_workspace_size", "attn_get_config", "attn_variants", "attn_strerror",
+    "library_path", "load_library",
 ]
 
 ATTN_F16 = 0
 ATTN_BF16 = 1
+ATTN_F32 = 2
 
 STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_DTYPE", -3: "ATTN_ERR_SHAPE",
@@ -46,6 +49,11 @@ class AttnError(RuntimeError):
 class attn_fwd_options(ctypes.Structure):
     _fields_ = [("rescale_threshold", ctypes.c_float), ("variant", ctypes.c_int),
                 ("grid", ctypes.c_int), ("reserved", ctypes.c_int * 4)]
+
+
+class attn_layout(ctypes.Structure):
+    _fields_ = [("batch_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("seq_stride", ctypes.c_int64)]
 
 
 class attn_config(ctypes.Structure):
@@ -79,6 +87,21 @@ def load_library(path: str | None = None):
         ip = ctypes.POINTER(ctypes.c_int)
         lib.attn_variant_info.argtypes = [i, ip, ip, ip, ip, ip, ip, ip]
         lib.attn_variant_info.restype = i
+        lp = ctypes.POINTER(attn_layout)
+        op = ctypes.POINTER(attn_fwd_options)
+        lib.attn_fwd_strided.argtypes = [vp, lp, vp, lp, vp, lp, vp, lp, vp, i, i, i, i, i, f, i,
+                                         vp, op]
+        lib.attn_fwd_strided.restype = i
+        lib.attn_fwd_partial.argtypes = [vp, lp, vp, lp, vp, lp, vp, vp, i, i, i, i, i, f, i, vp,
+                                         op]
+        lib.attn_fwd_partial.restype = i
+        lib.attn_merge.argtypes = [vp, vp, i, vp, lp, vp, i, i, i, i, i, vp]
+        lib.attn_merge.restype = i
+        lib.attn_fwd_split_workspace_size.argtypes = [i, i, i, i, i]
+        lib.attn_fwd_split_workspace_size.restype = ctypes.c_size_t
+        lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp,
+                                       ctypes.c_size_t, op]
+        lib.attn_fwd_split.restype = i
         lib.attn_strerror.argtypes = [i]
         lib.attn_strerror.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
@@ -189,3 +212,169 @@ def attn_variants() -> list:
         keys = ["id", "head_dim", "dtype", "block_m", "block_n", "waves", "stages"]
         out.append({kk: x.value for kk, x in zip(keys, vals)})
     return out
+
+
+def _layout(t):
+    """attn_layout of a [B, H, S, D] view whose last dimension is contiguous."""
+    if t.dim() != 4 or (t.shape[3] > 1 and t.stride(3) != 1):
+        raise ValueError("tensors must be [B, H, S, D] views with a contiguous last dimension")
+    return attn_layout(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _check_inputs(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Skv, D] with q's B, H and D")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype and device")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    return B, H, Sq, k.shape[2], D
+
+
+def _lse_buffer(lse, shape, device, required=False):
+    import torch
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if tuple(lse.shape) != tuple(shape) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != device:
+        raise ValueError(f"lse must be a contiguous float32 {tuple(shape)} tensor")
+    return lse
+
+
+def attn_fwd_strided(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_lse=True,
+                     rescale_threshold=None, variant=0, grid=0):
+    """Attention over strided [B, H, S, D] views (e.g. BSHD storage seen through
+    ``x.transpose(1, 2)``); k and v may have their own length Skv.
+
+    ``o`` may be any [B, H, Sq, D] view with a contiguous last dimension
+    (default: contiguous).  Returns (o, lse).
+    """
+    import torch
+
+    lib = load_library()
+    B, H, Sq, Skv, D = _check_inputs(q, k, v)
+    if o is None:
+        o = torch.empty((B, H, Sq, D), dtype=q.dtype, device=q.device)
+    elif tuple(o.shape) != (B, H, Sq, D) or o.dtype != q.dtype or o.device != q.device:
+        raise ValueError("o must be a [B, H, Sq, D] tensor of q's dtype")
+    if return_lse or lse is not None:
+        lse = _lse_buffer(lse, (B, H, Sq), q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    opts = _options(rescale_threshold, variant, grid)
+    ql, kl, vl, ol = _layout(q), _layout(k), _layout(v), _layout(o)
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_strided(q.data_ptr(), ctypes.byref(ql), k.data_ptr(), ctypes.byref(kl),
+                                  v.data_ptr(), ctypes.byref(vl), o.data_ptr(), ctypes.byref(ol),
+                                  lse.data_ptr() if lse is not None else None, B, H, Sq, Skv, D,
+                                  float(scale), _dtype_code(q), stream.cuda_stream,
+                                  ctypes.byref(opts))
+    _check(lib, st)
+    return o, lse
+
+
+def attn_fwd_partial(q, k, v, o_part=None, lse_part=None, scale=None, *, stream=None,
+                     rescale_threshold=None, variant=0, grid=0):
+    """Attention of q over the keys k, v of one range, as fp32 (o_part, lse_part):
+    o_part normalised within the range, lse_part = ln Σ_range exp(scale·q·k).
+    Inputs may be strided views (a key slice ``k[:, :, a:b]`` is one)."""
+    import torch
+
+    lib = load_library()
+    B, H, Sq, Skv, D = _check_inputs(q, k, v)
+    if o_part is None:
+        o_part = torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)
+    elif tuple(o_part.shape) != (B, H, Sq, D) or o_part.dtype != torch.float32 \
+            or not o_part.is_contiguous() or o_part.device != q.device:
+        raise ValueError("o_part must be a contiguous float32 [B, H, Sq, D] tensor")
+    lse_part = _lse_buffer(lse_part, (B, H, Sq), q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    opts = _options(rescale_threshold, variant, grid)
+    ql, kl, vl = _layout(q), _layout(k), _layout(v)
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_partial(q.data_ptr(), ctypes.byref(ql), k.data_ptr(), ctypes.byref(kl),
+                                  v.data_ptr(), ctypes.byref(vl), o_part.data_ptr(),
+                                  lse_part.data_ptr(), B, H, Sq, Skv, D, float(scale),
+                                  _dtype_code(q), stream.cuda_stream, ctypes.byref(opts))
+    _check(lib, st)
+    return o_part, lse_part
+
+
+def attn_merge(o_parts, lse_parts, o=None, lse=None, *, out_dtype=None, stream=None,
+               return_lse=True):
+    """Merges partials over disjoint key ranges: o_parts [n, B, H, S, D] fp32 and
+    lse_parts [n, B, H, S] fp32 (contiguous).  ``out_dtype`` is torch.float16,
+    torch.bfloat16 or torch.float32 (default float32 unless ``o`` is given)."""
+    import torch
+
+    lib = load_library()
+    if o_parts.dim() != 5 or o_parts.dtype != torch.float32 or not o_parts.is_contiguous():
+        raise ValueError("o_parts must be a contiguous float32 [n, B, H, S, D] tensor")
+    n, B, H, S, D = o_parts.shape
+    if tuple(lse_parts.shape) != (n, B, H, S) or lse_parts.dtype != torch.float32 \
+            or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be a contiguous float32 [n, B, H, S] tensor")
+    if o is None:
+        o = torch.empty((B, H, S, D), dtype=out_dtype or torch.float32, device=o_parts.device)
+    elif tuple(o.shape) != (B, H, S, D):
+        raise ValueError("o must be [B, H, S, D]")
+    code = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}[o.dtype]
+    if return_lse or lse is not None:
+        lse = _lse_buffer(lse, (B, H, S), o_parts.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(o_parts.device)
+    ol = _layout(o)
+    with torch.cuda.device(o_parts.device):
+        st = lib.attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), n, o.data_ptr(),
+                            ctypes.byref(ol), lse.data_ptr() if lse is not None else None,
+                            B, H, S, D, code, stream.cuda_stream)
+    _check(lib, st)
+    return o, lse
+
+
+def attn_fwd_split_workspace_size(B, H, S, D, kv_splits=0) -> int:
+    return int(load_library().attn_fwd_split_workspace_size(B, H, S, D, kv_splits))
+
+
+def attn_fwd_split(q, k, v, o=None, lse=None, scale=None, *, kv_splits=0, workspace=None,
+                   stream=None, return_lse=True, rescale_threshold=None, variant=0, grid=0):
+    """attn_fwd with the keys of each item split into kv_splits ranges (0 = the
+    library's choice) and merged; contiguous [B, H, S, D] tensors.  The fp32
+    workspace is allocated with torch when not given."""
+    import torch
+
+    lib = load_library()
+    B, H, S, Skv, D = _check_inputs(q, k, v)
+    if Skv != S or not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, S, D] tensors of one shape")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous tensor like q")
+    if return_lse or lse is not None:
+        lse = _lse_buffer(lse, (B, H, S), q.device)
+    need = attn_fwd_split_workspace_size(B, H, S, D, kv_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    opts = _options(rescale_threshold, variant, grid)
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, H, S, D,
+                                float(scale), _dtype_code(q), stream.cuda_stream, int(kv_splits),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                ctypes.byref(opts))
+    _check(lib, st)
+    return o, lse

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = [os.path.join(CSRC, "attn_api.hip")]
-HEADERS = [os.path.join(CSRC, "attn_fwd_kernel.h"), os.path.join(INCLUDE, "attn.h")]
+HEADERS = [os.path.join(CSRC, "attn_fwd_kernel.h"), os.path.join(CSRC, "attn_merge_kernel.h"),
+           os.path.join(INCLUDE, "attn.h")]
 
 
 def hipcc() -> str:

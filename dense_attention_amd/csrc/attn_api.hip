@@ -1,6 +1,7 @@
 // C ABI of the fused dense attention forward (declared in include/attn.h):
-// argument validation, tile-variant choice, persistent-grid sizing and the
-// launch on the caller's stream.  No allocation, no synchronisation.
+// argument validation, tile-variant choice, persistent-grid sizing, KV-range
+// splitting and the launches on the caller's stream.  No allocation, no
+// synchronisation.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -11,6 +12,7 @@
 
 #include "attn.h"
 #include "attn_fwd_kernel.h"
+#include "attn_merge_kernel.h"
 
 namespace {
 
@@ -79,10 +81,6 @@ const Variant kVariants[] = {
     make_variant<F16, ATTN_F16, Tile<128, 64, 4, 1>>(6),
     make_variant<BF16, ATTN_BF16, Tile<64, 64, 8, 1>>(7),
     make_variant<F16, ATTN_F16, Tile<64, 64, 8, 1>>(8),
-    make_variant<BF16, ATTN_BF16, Tile<128, 128, 4, 1>>(9),
-    make_variant<F16, ATTN_F16, Tile<128, 128, 4, 1>>(10),
-    make_variant<BF16, ATTN_BF16, Tile<128, 64, 4, 2>>(11),
-    make_variant<F16, ATTN_F16, Tile<128, 64, 4, 2>>(12),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -134,6 +132,8 @@ struct Plan {
   const Variant* var = nullptr;
   int var_index = 0;
   int n_qtiles = 0;
+  int n_splits = 1;
+  int split_len = 0;
   int n_items = 0;
   int grid = 0;
   int per_cu = 0;
@@ -142,13 +142,19 @@ struct Plan {
   bool empty = false;
 };
 
-// Validation shared by every entry point (data pointers excluded).
-int plan_launch(int B, int H, int S, int D, int dtype, float scale,
-                const attn_fwd_options_t* opts, bool need_device, Plan* plan) {
+constexpr int kMaxSplits = 64;
+constexpr int kMinSplitKeys = 256;
+
+// Validation shared by every forward entry point (data pointers excluded).
+// kv_splits: 1 = one range per item, 0 = choose to fill the device (needs the
+// device), n > 1 = at most n ranges.
+int plan_launch(int B, int H, int Sq, int Skv, int D, int dtype, float scale,
+                const attn_fwd_options_t* opts, int kv_splits, bool need_device, Plan* plan) {
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return fail(ATTN_ERR_DTYPE, "dtype must be ATTN_F16 or ATTN_BF16");
-  if (B < 0 || H < 0 || S < 0) return fail(ATTN_ERR_SHAPE, "B, H and S must be >= 0");
+  if (B < 0 || H < 0 || Sq < 0 || Skv < 0) return fail(ATTN_ERR_SHAPE, "B, H and S must be >= 0");
   if (D != 64 && D != 128) return fail(ATTN_ERR_SHAPE, "D must be 64 or 128");
   if (!std::isfinite(scale)) return fail(ATTN_ERR_SCALE, "scale must be finite");
+  if (kv_splits < 0 || kv_splits > kMaxSplits) return fail(ATTN_ERR_ARG, "kv_splits must be in [0, 64]");
   if (opts) {
     for (int r : opts->reserved)
       if (r != 0) return fail(ATTN_ERR_ARG, "reserved option fields must be zero");
@@ -156,10 +162,10 @@ int plan_launch(int B, int H, int S, int D, int dtype, float scale,
     if (!(opts->rescale_threshold <= 64.0f) && !(opts->rescale_threshold < 0.0f))
       return fail(ATTN_ERR_ARG, "rescale_threshold must be <= 64");
   }
-  // 64-bit element offsets are used per head; a single head and the item count
-  // must fit in 32-bit indices.
-  if ((int64_t)S * D >= (int64_t)1 << 31) return fail(ATTN_ERR_SHAPE, "S*D must be < 2^31");
-  if ((int64_t)B * H * (int64_t)S >= (int64_t)1 << 31) return fail(ATTN_ERR_SHAPE, "B*H*S must be < 2^31");
+  // Rows are indexed with 32-bit integers inside a head and work items with
+  // 32-bit integers overall.
+  if ((int64_t)B * H * (int64_t)Sq >= (int64_t)1 << 31 || Skv >= (1 << 30))
+    return fail(ATTN_ERR_SHAPE, "B*H*Sq must be < 2^31 and Skv < 2^30");
 
   const Variant* var = default_variant(D, dtype);
   if (opts && opts->variant != 0) {
@@ -170,21 +176,181 @@ int plan_launch(int B, int H, int S, int D, int dtype, float scale,
   plan->var = var;
   plan->var_index = (int)(var - kVariants);
   plan->thr = (opts && opts->rescale_threshold >= 0.0f) ? opts->rescale_threshold : kDefaultThreshold;
-  plan->n_qtiles = (S + var->block_m - 1) / var->block_m;
-  plan->n_items = B * H * plan->n_qtiles;
-  plan->empty = (plan->n_items == 0);
-  if (!need_device) return ATTN_OK;
+  plan->n_qtiles = (Sq + var->block_m - 1) / var->block_m;
+  plan->empty = ((int64_t)B * H * plan->n_qtiles == 0);
+  if (!plan->empty && Skv == 0) return fail(ATTN_ERR_SHAPE, "queries need at least one key (Skv >= 1)");
+  const int base_items = B * H * plan->n_qtiles;
 
   const DeviceInfo* di = nullptr;
-  int st = device_info(&di);
-  if (st != ATTN_OK) return st;
-  plan->num_cus = di->num_cus;
-  plan->per_cu = di->occupancy[plan->var_index];
+  if (need_device || kv_splits == 0) {
+    int st = device_info(&di);
+    if (st != ATTN_OK) return st;
+    plan->num_cus = di->num_cus;
+    plan->per_cu = di->occupancy[plan->var_index];
+  }
+  // KV ranges: whole tiles, at least kMinSplitKeys keys each when chosen here.
+  int want = kv_splits;
+  if (want == 0) {
+    const int slots = plan->num_cus * plan->per_cu;
+    want = base_items > 0 ? (slots + base_items - 1) / base_items : 1;
+    const int max_by_len = Skv / kMinSplitKeys > 0 ? Skv / kMinSplitKeys : 1;
+    if (want > max_by_len) want = max_by_len;
+    if (want > kMaxSplits) want = kMaxSplits;
+  }
+  if (want < 1) want = 1;
+  const int bn = var->block_n;
+  int len = (Skv + want - 1) / want;
+  len = ((len + bn - 1) / bn) * bn;
+  if (len < bn) len = bn;
+  plan->split_len = want == 1 ? (Skv > 0 ? Skv : 1) : len;
+  plan->n_splits = want == 1 ? 1 : (Skv + len - 1) / len;
+  if ((int64_t)base_items * plan->n_splits >= (int64_t)1 << 31) return fail(ATTN_ERR_SHAPE, "too many work items");
+  plan->n_items = base_items * plan->n_splits;
+  if (!need_device) return ATTN_OK;
+
   int grid = di->num_cus * plan->per_cu;
   if (opts && opts->grid > 0) grid = opts->grid;
   if (grid > plan->n_items) grid = plan->n_items;
   plan->grid = grid;
   return ATTN_OK;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+attn_layout_t contiguous(int H, int S, int D) {
+  return attn_layout_t{(int64_t)H * S * D, (int64_t)S * D, (int64_t)D};
+}
+
+int check_layout(const attn_layout_t& l, const char* what) {
+  if (l.batch_stride < 0 || l.head_stride < 0 || l.seq_stride < 0 ||
+      (l.batch_stride % 8) != 0 || (l.head_stride % 8) != 0 || (l.seq_stride % 8) != 0) {
+    char buf[128];
+    std::snprintf(buf, sizeof(buf), "%s strides must be >= 0 and multiples of 8 elements", what);
+    return fail(ATTN_ERR_SHAPE, buf);
+  }
+  if (l.seq_stride >= (1 << 24)) {
+    char buf[128];
+    std::snprintf(buf, sizeof(buf), "%s seq_stride must be < 2^24", what);
+    return fail(ATTN_ERR_SHAPE, buf);
+  }
+  return ATTN_OK;
+}
+
+// One forward launch: inputs with their layouts, the output (dtype or fp32
+// partials) and the KV-range split.
+struct Forward {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  void* o = nullptr;
+  float* lse = nullptr;
+  attn_layout_t ql{}, kl{}, vl{}, ol{};
+  int B = 0, H = 0, Sq = 0, Skv = 0, D = 0;
+  float scale = 0.f;
+  int dtype = 0;
+  bool o_f32 = false;
+  long long o_split = 0, lse_split = 0;
+};
+
+int check_pointers(const Forward& f) {
+  if (!f.q || !f.k || !f.v || !f.o) return fail(ATTN_ERR_NULL, "q, k, v and o must be non-null");
+  if (misaligned(f.q, 16) || misaligned(f.k, 16) || misaligned(f.v, 16) || misaligned(f.o, 16))
+    return fail(ATTN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (f.lse && misaligned(f.lse, 4)) return fail(ATTN_ERR_ALIGN, "lse must be 4-byte aligned");
+  int st;
+  if ((st = check_layout(f.ql, "q")) != ATTN_OK) return st;
+  if ((st = check_layout(f.kl, "k")) != ATTN_OK) return st;
+  if ((st = check_layout(f.vl, "v")) != ATTN_OK) return st;
+  if ((st = check_layout(f.ol, "o")) != ATTN_OK) return st;
+  if (f.ol.seq_stride < f.D) return fail(ATTN_ERR_SHAPE, "o seq_stride must be >= D");
+  return ATTN_OK;
+}
+
+int launch_forward(const Forward& f, const Plan& plan, hipStream_t stream) {
+  Params p;
+  p.q = static_cast<const uint16_t*>(f.q);
+  p.k = static_cast<const uint16_t*>(f.k);
+  p.v = static_cast<const uint16_t*>(f.v);
+  p.o = f.o;
+  p.lse = f.lse;
+  p.q_sb = f.ql.batch_stride; p.q_sh = f.ql.head_stride; p.q_ss = (int)f.ql.seq_stride;
+  p.k_sb = f.kl.batch_stride; p.k_sh = f.kl.head_stride; p.k_ss = (int)f.kl.seq_stride;
+  p.v_sb = f.vl.batch_stride; p.v_sh = f.vl.head_stride; p.v_ss = (int)f.vl.seq_stride;
+  p.o_sb = f.ol.batch_stride; p.o_sh = f.ol.head_stride; p.o_ss = (int)f.ol.seq_stride;
+  p.o_split = f.o_split;
+  p.lse_split = f.lse_split;
+  p.H = f.H;
+  p.BH = f.B * f.H;
+  p.Sq = f.Sq;
+  p.Skv = f.Skv;
+  p.n_qtiles = plan.n_qtiles;
+  p.n_splits = plan.n_splits;
+  p.split_len = plan.split_len;
+  p.n_items = plan.n_items;
+  p.xcd_remap = (plan.grid % 8 == 0 && plan.grid >= 8) ? 1 : 0;
+  p.o_f32 = f.o_f32 ? 1 : 0;
+  p.c = f.scale * kLog2e;
+  p.thr = plan.thr;
+  hipError_t e = plan.var->launch(p, p.c < 0.0f, plan.grid, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+template <class T, int D>
+hipError_t merge_launch(const attn::MergeParams& m, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 8);
+  const long long blocks = (m.rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((attn::attn_merge_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
+int launch_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o,
+                 const attn_layout_t& ol, float* lse, int B, int H, int S, int D, int dtype,
+                 hipStream_t stream) {
+  attn::MergeParams m;
+  m.o_parts = o_parts;
+  m.lse_parts = lse_parts;
+  m.o = o;
+  m.lse = lse;
+  m.o_sb = ol.batch_stride;
+  m.o_sh = ol.head_stride;
+  m.o_ss = (int)ol.seq_stride;
+  m.n_parts = n_parts;
+  m.H = H;
+  m.S = S;
+  m.rows = (long long)B * H * S;
+  m.part_stride = m.rows * D;
+  m.f32_out = dtype == ATTN_F32 ? 1 : 0;
+  if (m.rows / (256 / (D / 8)) >= (1LL << 31)) return fail(ATTN_ERR_SHAPE, "too many rows to merge");
+  hipError_t e;
+  if (dtype == ATTN_F16)
+    e = D == 64 ? merge_launch<F16, 64>(m, stream) : merge_launch<F16, 128>(m, stream);
+  else
+    e = D == 64 ? merge_launch<BF16, 64>(m, stream) : merge_launch<BF16, 128>(m, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+// Workspace of attn_fwd_split: fp32 partial O then fp32 partial LSE, each
+// 256-byte aligned.
+size_t split_o_bytes(int B, int H, int S, int D, int n) {
+  size_t b = (size_t)n * B * H * S * D * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+size_t split_ws_bytes(int B, int H, int S, int D, int n) {
+  size_t l = (size_t)n * B * H * S * sizeof(float);
+  return split_o_bytes(B, H, S, D, n) + ((l + 255) & ~(size_t)255);
+}
+
+int forward(const Forward& f, const attn_fwd_options_t* opts, hipStream_t stream) {
+  Plan plan;
+  int st = plan_launch(f.B, f.H, f.Sq, f.Skv, f.D, f.dtype, f.scale, opts, 1, /*need_device=*/false, &plan);
+  if (st != ATTN_OK) return st;
+  if (plan.empty) return ATTN_OK;
+  if ((st = check_pointers(f)) != ATTN_OK) return st;
+  st = plan_launch(f.B, f.H, f.Sq, f.Skv, f.D, f.dtype, f.scale, opts, 1, /*need_device=*/true, &plan);
+  if (st != ATTN_OK) return st;
+  return launch_forward(f, plan, stream);
 }
 
 }  // namespace
@@ -195,33 +361,11 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int S, int D, float scale, int dtype, void* stream,
                 const attn_fwd_options_t* opts) {
   g_last_error[0] = '\0';
-  Plan plan;
-  int st = plan_launch(B, H, S, D, dtype, scale, opts, /*need_device=*/false, &plan);
-  if (st != ATTN_OK) return st;
-  if (plan.empty) return ATTN_OK;
-  if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "q, k, v and o must be non-null");
-  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
-    return fail(ATTN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
-  if (lse && misaligned(lse, 4)) return fail(ATTN_ERR_ALIGN, "lse must be 4-byte aligned");
-  st = plan_launch(B, H, S, D, dtype, scale, opts, /*need_device=*/true, &plan);
-  if (st != ATTN_OK) return st;
-
-  Params p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<uint16_t*>(o);
-  p.lse = lse;
-  p.S = S;
-  p.n_qtiles = plan.n_qtiles;
-  p.n_items = plan.n_items;
-  p.xcd_remap = (plan.grid % 8 == 0 && plan.grid >= 8) ? 1 : 0;
-  p.c = scale * kLog2e;
-  p.thr = plan.thr;
-  hipError_t e = plan.var->launch(p, p.c < 0.0f, plan.grid, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, hipGetErrorString(e));
-  return ATTN_OK;
+  Forward f;
+  f.q = q; f.k = k; f.v = v; f.o = o; f.lse = lse;
+  f.B = B; f.H = H; f.Sq = S; f.Skv = S; f.D = D; f.scale = scale; f.dtype = dtype;
+  f.ql = f.kl = f.vl = f.ol = contiguous(H, S, D);
+  return forward(f, opts, static_cast<hipStream_t>(stream));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -229,12 +373,121 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return attn_fwd_ex(q, k, v, o, lse, B, H, S, D, scale, dtype, stream, nullptr);
 }
 
+int attn_fwd_strided(const void* q, const attn_layout_t* q_layout, const void* k,
+                     const attn_layout_t* k_layout, const void* v, const attn_layout_t* v_layout,
+                     void* o, const attn_layout_t* o_layout, float* lse, int B, int H, int Sq,
+                     int Skv, int D, float scale, int dtype, void* stream,
+                     const attn_fwd_options_t* opts) {
+  g_last_error[0] = '\0';
+  Forward f;
+  f.q = q; f.k = k; f.v = v; f.o = o; f.lse = lse;
+  f.B = B; f.H = H; f.Sq = Sq; f.Skv = Skv; f.D = D; f.scale = scale; f.dtype = dtype;
+  f.ql = q_layout ? *q_layout : contiguous(H, Sq, D);
+  f.kl = k_layout ? *k_layout : contiguous(H, Skv, D);
+  f.vl = v_layout ? *v_layout : contiguous(H, Skv, D);
+  f.ol = o_layout ? *o_layout : contiguous(H, Sq, D);
+  return forward(f, opts, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_partial(const void* q, const attn_layout_t* q_layout, const void* k,
+                     const attn_layout_t* k_layout, const void* v, const attn_layout_t* v_layout,
+                     float* o_part, float* lse_part, int B, int H, int Sq, int Skv, int D,
+                     float scale, int dtype, void* stream, const attn_fwd_options_t* opts) {
+  g_last_error[0] = '\0';
+  Forward f;
+  f.q = q; f.k = k; f.v = v; f.o = o_part; f.lse = lse_part;
+  f.B = B; f.H = H; f.Sq = Sq; f.Skv = Skv; f.D = D; f.scale = scale; f.dtype = dtype;
+  f.ql = q_layout ? *q_layout : contiguous(H, Sq, D);
+  f.kl = k_layout ? *k_layout : contiguous(H, Skv, D);
+  f.vl = v_layout ? *v_layout : contiguous(H, Skv, D);
+  f.ol = contiguous(H, Sq, D);
+  f.o_f32 = true;
+  Plan plan;
+  int st = plan_launch(B, H, Sq, Skv, D, dtype, scale, opts, 1, /*need_device=*/false, &plan);
+  if (st != ATTN_OK) return st;
+  if (plan.empty) return ATTN_OK;
+  if (!lse_part) return fail(ATTN_ERR_NULL, "lse_part must be non-null");
+  return forward(f, opts, static_cast<hipStream_t>(stream));
+}
+
+int attn_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o,
+               const attn_layout_t* o_layout, float* lse, int B, int H, int S, int D, int dtype,
+               void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_F32)
+    return fail(ATTN_ERR_DTYPE, "dtype must be ATTN_F16, ATTN_BF16 or ATTN_F32");
+  if (B < 0 || H < 0 || S < 0) return fail(ATTN_ERR_SHAPE, "B, H and S must be >= 0");
+  if (D != 64 && D != 128) return fail(ATTN_ERR_SHAPE, "D must be 64 or 128");
+  if (n_parts < 1) return fail(ATTN_ERR_ARG, "n_parts must be >= 1");
+  if ((int64_t)B * H * S >= (int64_t)1 << 31) return fail(ATTN_ERR_SHAPE, "B*H*S must be < 2^31");
+  if ((int64_t)B * H * S == 0) return ATTN_OK;
+  if (!o_parts || !lse_parts || !o) return fail(ATTN_ERR_NULL, "o_parts, lse_parts and o must be non-null");
+  if (misaligned(o_parts, 16) || misaligned(o, 16) || misaligned(lse_parts, 4) || (lse && misaligned(lse, 4)))
+    return fail(ATTN_ERR_ALIGN, "o_parts and o must be 16-byte aligned, lse arrays 4-byte aligned");
+  const attn_layout_t ol = o_layout ? *o_layout : contiguous(H, S, D);
+  int st = check_layout(ol, "o");
+  if (st != ATTN_OK) return st;
+  if (ol.seq_stride < D) return fail(ATTN_ERR_SHAPE, "o seq_stride must be >= D");
+  const DeviceInfo* di = nullptr;
+  if ((st = device_info(&di)) != ATTN_OK) return st;
+  return launch_merge(o_parts, lse_parts, n_parts, o, ol, lse, B, H, S, D, dtype,
+                      static_cast<hipStream_t>(stream));
+}
+
+size_t attn_fwd_split_workspace_size(int B, int H, int S, int D, int kv_splits) {
+  if (B < 0 || H < 0 || S < 0 || (D != 64 && D != 128) || kv_splits < 0 || kv_splits > kMaxSplits) return 0;
+  // With kv_splits == 0 the library may choose up to kMaxSplits ranges, but
+  // never more than S / kMinSplitKeys (and at least one).
+  int n = kv_splits;
+  if (n == 0) {
+    n = S / kMinSplitKeys;
+    if (n > kMaxSplits) n = kMaxSplits;
+  }
+  if (n < 1) n = 1;
+  return split_ws_bytes(B, H, S, D, n);
+}
+
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int S, int D, float scale, int dtype, void* stream, int kv_splits,
+                   void* workspace, size_t workspace_bytes, const attn_fwd_options_t* opts) {
+  g_last_error[0] = '\0';
+  Plan plan;
+  int st = plan_launch(B, H, S, S, D, dtype, scale, opts, kv_splits == 0 ? 1 : kv_splits,
+                       /*need_device=*/false, &plan);
+  if (st != ATTN_OK) return st;
+  if (plan.empty) return ATTN_OK;
+  Forward f;
+  f.q = q; f.k = k; f.v = v; f.o = o; f.lse = lse;
+  f.B = B; f.H = H; f.Sq = S; f.Skv = S; f.D = D; f.scale = scale; f.dtype = dtype;
+  f.ql = f.kl = f.vl = f.ol = contiguous(H, S, D);
+  if ((st = check_pointers(f)) != ATTN_OK) return st;
+  st = plan_launch(B, H, S, S, D, dtype, scale, opts, kv_splits, /*need_device=*/true, &plan);
+  if (st != ATTN_OK) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (plan.n_splits == 1) return launch_forward(f, plan, hs);
+  const size_t need = split_ws_bytes(B, H, S, D, plan.n_splits);
+  if (!workspace) return fail(ATTN_ERR_NULL, "workspace must be non-null");
+  if (misaligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need) return fail(ATTN_ERR_ARG, "workspace is smaller than attn_fwd_split_workspace_size()");
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_o_bytes(B, H, S, D, plan.n_splits));
+  Forward part = f;
+  part.o = o_parts;
+  part.lse = lse_parts;
+  part.ol = contiguous(H, S, D);
+  part.o_f32 = true;
+  part.o_split = (long long)B * H * S * D;
+  part.lse_split = (long long)B * H * S;
+  if ((st = launch_forward(part, plan, hs)) != ATTN_OK) return st;
+  return launch_merge(o_parts, lse_parts, plan.n_splits, o, f.ol, lse, B, H, S, D, dtype, hs);
+}
+
 int attn_get_config(int B, int H, int S, int D, int dtype, const attn_fwd_options_t* opts,
                     attn_config_t* out) {
   g_last_error[0] = '\0';
   if (!out) return fail(ATTN_ERR_NULL, "out must be non-null");
   Plan plan;
-  int st = plan_launch(B, H, S, D, dtype, 1.0f, opts, /*need_device=*/true, &plan);
+  int st = plan_launch(B, H, S, S, D, dtype, 1.0f, opts, 1, /*need_device=*/true, &plan);
   if (st != ATTN_OK) return st;
   out->variant = plan.var->id;
   out->block_m = plan.var->block_m;

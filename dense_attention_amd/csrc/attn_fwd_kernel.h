@@ -78,19 +78,33 @@ struct Mma<F16> {
   }
 };
 
-// Kernel arguments (by value).
+// Kernel arguments (by value).  Strides are in elements; the head dimension
+// is contiguous.  Work item = (b·H + h, query tile, KV range).
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  uint16_t* o;
-  float* lse;        // may be null
-  int S;             // sequence length
-  int n_qtiles;      // ceil(S / BM)
-  int n_items;       // B * H * n_qtiles
-  int xcd_remap;     // 1: the grid is a multiple of 8, group items per XCD
-  float c;           // scale * log2(e): scores in log2 units are s * c
-  float thr;         // lazy-rescale threshold (log2 units)
+  void* o;               // T elements, or fp32 when o_f32
+  float* lse;            // contiguous [.., B, H, Sq]; may be null
+  long long q_sb, q_sh;  // batch and head strides
+  long long k_sb, k_sh;
+  long long v_sb, v_sh;
+  long long o_sb, o_sh;
+  long long o_split;     // elements between the outputs of consecutive KV ranges
+  long long lse_split;
+  int q_ss, k_ss, v_ss, o_ss;  // row (token) strides
+  int H;
+  int BH;                // B * H
+  int Sq;                // query rows per head
+  int Skv;               // keys per head
+  int n_qtiles;          // ceil(Sq / BM)
+  int n_splits;          // KV ranges per (head, query tile)
+  int split_len;         // keys per range (a multiple of BN; the last may be shorter)
+  int n_items;           // B * H * n_qtiles * n_splits
+  int xcd_remap;         // 1: the grid is a multiple of 8, group items per XCD
+  int o_f32;             // 1: O is stored in fp32, normalised within its KV range
+  float c;               // scale * log2(e): scores in log2 units are s * c
+  float thr;             // lazy-rescale threshold (log2 units)
 };
 
 // MFMA row r of a 32-row block -> row of the K tile (or head-dim index of the
@@ -112,7 +126,7 @@ struct Tile {
   static constexpr int VS = D * 2 + 64;     // LDS row stride of V (bytes)
   static constexpr int K_TILE = BN * KS;
   static constexpr int V_TILE = BN * VS;
-  static constexpr int STAGES = 2;           // two K and two V buffers
+  static constexpr int STAGES = 3;           // three K and three V buffers
   static constexpr int LDS_BYTES = STAGES * (K_TILE + V_TILE);
   // Waves per SIMD the register allocation targets.
   static constexpr int WPE = NW / 4;
@@ -142,7 +156,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const lds
 // padded LDS tile of row stride STRIDE.  Each wave owns BPW of the tile's
 // 1 KiB blocks; lane i of a block fills 16-byte slot i.  With LANE_ORDER, LDS
 // row p of each 32-row block receives key lane_key(p).  Pad slots are not
-// loaded.  The per-lane element offsets do not depend on the tile, so they are
+// loaded.  The per-lane byte offsets do not depend on the tile, so they are
 // computed once per kernel and a full tile costs one address add per block.
 template <class TL, int STRIDE, bool LANE_ORDER>
 struct DmaPlan {
@@ -161,17 +175,17 @@ struct DmaPlan {
     key = LANE_ORDER ? ((p & ~31) | lane_key(p & 31)) : p;
   }
 
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // row_bytes: distance of consecutive rows in bytes (BN·row_bytes < 2^31).
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes) {
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
       int key, c;
       slot_rc(wave * BPW + t, lane, key, c);
-      off[t] = (uint32_t)(key * TL::D + c * 8) * 2u;
+      off[t] = (uint32_t)key * row_bytes + (uint32_t)c * 16u;
     }
   }
 
-  // Full tile starting at element `tile` (= head + kb·D).  `blk < BLOCKS` is
-  // wave-uniform.
+  // Full tile whose first row is at `tile`.  `blk < BLOCKS` is wave-uniform.
   __device__ __forceinline__ void issue(const uint16_t* tile, lds_t* dst, int wave) const {
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
@@ -184,22 +198,20 @@ struct DmaPlan {
     }
   }
 
-  // Tile that may run past row S-1: such rows are clamped to row S-1 (their
-  // scores are masked and their P is 0).  The row is recovered from the offset
-  // (a row is 2·D bytes, a power of two).
-  __device__ __forceinline__ void issue_clamped(const uint16_t* head, int kb, int S, lds_t* dst,
-                                                int wave) const {
-    constexpr int ROW_BYTES = 2 * TL::D;
-    constexpr int ROW_SHIFT = ROW_BYTES == 256 ? 8 : 7;
-    static_assert(ROW_BYTES == (1 << ROW_SHIFT), "row size");
+  // Tile whose first row is at `tile` and that may run past the last key: its
+  // rows at or beyond `rows` are clamped to row rows-1 (their scores are
+  // masked and their P is 0).  Rare (last tile of a ragged range), so the
+  // lane's row is recomputed here instead of being kept in registers.
+  __device__ __forceinline__ void issue_clamped(const uint16_t* tile, int rows, uint32_t row_bytes,
+                                                lds_t* dst, int wave, int lane) const {
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
       const int blk = wave * BPW + t;
       if (BLOCKS % TL::NW == 0 || blk < BLOCKS) {
-        const uint32_t o = off[t];
-        const int row = min(kb + (int)(o >> ROW_SHIFT), S - 1);
-        // Uniform base of row 0 plus a per-lane byte offset (rows < 2^23).
-        dma16(head, (uint32_t)row * ROW_BYTES + (o & (ROW_BYTES - 1)), dst + blk * 1024);
+        int key, c;
+        slot_rc(blk, lane, key, c);
+        key = min(key, rows - 1);
+        dma16(tile, (uint32_t)key * row_bytes + (uint32_t)c * 16u, dst + blk * 1024);
       }
     }
   }
@@ -285,11 +297,19 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
   // lane group g = lane/16 covers key half g/2 and head-dim half g%2; inside
   // the group, lane i reads key row i/4 and the 8-byte piece of head-dim
   // columns chosen so that the result is lane_key-ordered.
-  const lds_t* kbase = kl + (lane & 31) * TL::KS + (lane >> 5) * 16;
+  // The two bases are made opaque once per step: every operand read is then
+  // base + immediate, instead of an address the compiler rebuilds from the
+  // (runtime) ring slot before each read.
   const int g = lane >> 4;
   const int li = lane & 15;
-  const lds_t* vbase = vl + (16 * (g >> 1) + (li >> 2)) * TL::VS +
-                       (2 * (li & 1) + (g & 1)) * 16 + ((li >> 1) & 1) * 8;
+  uint32_t ka = (uint32_t)(uintptr_t)kl + (uint32_t)((lane & 31) * TL::KS + (lane >> 5) * 16);
+  uint32_t va = (uint32_t)(uintptr_t)vl + (uint32_t)((16 * (g >> 1) + (li >> 2)) * TL::VS +
+                                                      (2 * (li & 1) + (g & 1)) * 16 +
+                                                      ((li >> 1) & 1) * 8);
+  if (QK) asm volatile("" : "+v"(ka));
+  if (PV) asm volatile("" : "+v"(va));
+  const lds_t* kbase = (const lds_t*)(uintptr_t)ka;
+  const lds_t* vbase = (const lds_t*)(uintptr_t)va;
 
   auto kfrag = [&](int i) -> u32x4_t {
     return ld_lds16(kbase + (i / DT) * 32 * TL::KS + (i % DT) * 32);
@@ -443,14 +463,14 @@ __device__ __forceinline__ void rescale_o(WaveState<TL>& ws, const float (&alpha
       for (int i = 0; i < 16; ++i) ws.o[qb][db][i] *= alpha[qb];
 }
 
-// LDS ring: two K buffers then two V buffers; K_t lives in K buffer t%2 and V_t
-// in V buffer t%2.
+// LDS ring: three K buffers then three V buffers; K_t lives in K buffer t%3
+// and V_t in V buffer t%3.
 template <class TL>
 struct Ring {
   lds_t* base;
-  __device__ __forceinline__ lds_t* k(int t) const { return base + (t & 1) * TL::K_TILE; }
+  __device__ __forceinline__ lds_t* k(int t) const { return base + (t % 3) * TL::K_TILE; }
   __device__ __forceinline__ lds_t* v(int t) const {
-    return base + 2 * TL::K_TILE + (t & 1) * TL::V_TILE;
+    return base + 3 * TL::K_TILE + (t % 3) * TL::V_TILE;
   }
 };
 
@@ -460,35 +480,50 @@ struct Copies {
   DmaPlan<TL, TL::VS, false> v;
 };
 
-// Epilogue of a work item: O / l rounded to the output type, and the LSE.
+// Epilogue of a work item: O / l (rounded to the output type, or fp32 for a
+// partial result over one KV range) and the LSE.
 template <class T, class TL>
-__device__ __forceinline__ void store_output(const Params& p, const WaveState<TL>& ws, size_t head,
-                                             int bh, int qt, int wave, int lane) {
-  constexpr int D = TL::D, QB = TL::QB, DB = D / 32;
+__device__ __forceinline__ void store_output(const Params& p, const WaveState<TL>& ws,
+                                             long long o_off, long long lse_off, int qt, int wave,
+                                             int lane) {
+  constexpr int QB = TL::QB, DB = TL::D / 32;
   const int lr = lane & 31;
   const int hh = lane >> 5;
-  const int S = p.S;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lane_pair_sum(ws.l[qb]);
     const int row = qt * TL::BM + (wave * QB + qb) * 32 + lr;
-    if (row < S) {
+    if (row < p.Sq) {
       const float inv = 1.0f / lt;
-      uint16_t* orow = p.o + head + (size_t)row * D;
+      const long long ro = o_off + (long long)row * p.o_ss;
+      if (p.o_f32) {
+        float* orow = static_cast<float*>(p.o) + ro;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        uint32_t w[8];
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          w[i] = Mma<T>::pack(ws.o[qb][db][2 * i] * inv, ws.o[qb][db][2 * i + 1] * inv);
-        u32x4_t w0 = {w[0], w[1], w[2], w[3]};
-        u32x4_t w1 = {w[4], w[5], w[6], w[7]};
-        *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh) = w0;
-        *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh + 8) = w1;
+          for (int j = 0; j < 4; ++j) {
+            u32x4_t w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(uint32_t, ws.o[qb][db][4 * j + e] * inv);
+            *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh + 4 * j) = w;
+          }
+      } else {
+        uint16_t* orow = static_cast<uint16_t*>(p.o) + ro;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          uint32_t w[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            w[i] = Mma<T>::pack(ws.o[qb][db][2 * i] * inv, ws.o[qb][db][2 * i + 1] * inv);
+          u32x4_t w0 = {w[0], w[1], w[2], w[3]};
+          u32x4_t w1 = {w[4], w[5], w[6], w[7]};
+          *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh) = w0;
+          *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh + 8) = w1;
+        }
       }
       if (p.lse != nullptr && hh == 0) {
         // ln(sum_j exp(s_j * scale)) = (m + log2(l)) * ln 2
-        p.lse[(size_t)bh * S + row] = (ws.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
+        p.lse[lse_off + row] = (ws.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
       }
     }
   }
@@ -508,10 +543,10 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
 // Attention Kernel from Scratch to Near-SOTA in 60 Diagrams", Chapter 4 - Warp
 // Specialization, and "Attention for sm90, Line by Line", "Why does a flash
 // attention kernel need three warpgroups?", obtain with separate roles).
-// Copies: in slot 2i every wave issues its share of K_{i+1} and V_i, and
-// waits for them at the end of slot 2i+1.  K_i is read in slots 2i and 2i+1
-// and V_{i-1} in the same two slots, so a buffer refilled in slot 2i+2 (two
-// tiles later) is no longer read.
+// K/V copies are issued and awaited only in VALU phases (and, for group 1, at
+// the end of an MFMA phase), so the MFMA phase issues nothing but MFMAs and
+// their LDS operand reads; the three-deep ring makes that legal (see
+// process_item).
 
 template <class T, class TL, bool QK, bool PV, bool NEG>
 __device__ __forceinline__ void mfma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
@@ -537,46 +572,57 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, DB = D / 32, DT = D / 16;
   const int lr = lane & 31;
   const int hh = lane >> 5;
-  // S passes through an empty asm so that per-lane values derived from it
-  // (tail masks, clamped copy addresses) are recomputed per item instead of
-  // being hoisted out of the persistent loop, where they would occupy
-  // registers for the whole kernel.
-  int S = p.S;
+  // Item -> (KV range sp, head bh, query tile qt); consecutive items are the
+  // query tiles of one head and one KV range.
+  const int qt = item % p.n_qtiles;
+  const int t_ = item / p.n_qtiles;
+  const int bh = t_ % p.BH;
+  const int sp = t_ / p.BH;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int k0 = sp * p.split_len;
+  // S (keys of this item's range) passes through an empty asm so that per-lane
+  // values derived from it (tail masks, clamped copy addresses) are recomputed
+  // per item instead of being hoisted out of the persistent loop, where they
+  // would occupy registers for the whole kernel.
+  int S = min(p.Skv - k0, p.split_len);
   asm volatile("" : "+s"(S));
   const float c = p.c, thr = p.thr;
   const int grp = TL::NW == 8 ? (wave >> 2) : 0;
+  const int kss = p.k_ss, vss = p.v_ss;
+  const uint32_t krb = (uint32_t)kss * 2u, vrb = (uint32_t)vss * 2u;
 
-  const int bh = item / p.n_qtiles;
-  const int qt = item - bh * p.n_qtiles;
-  const size_t head = (size_t)bh * (size_t)S * D;
-  const uint16_t* __restrict__ qh = p.q + head;
-  const uint16_t* __restrict__ kh = p.k + head;
-  const uint16_t* __restrict__ vh = p.v + head;
+  const uint16_t* __restrict__ qh = p.q + b * p.q_sb + h * p.q_sh;
+  const uint16_t* __restrict__ kh = p.k + b * p.k_sb + h * p.k_sh + (long long)k0 * kss;
+  const uint16_t* __restrict__ vh = p.v + b * p.v_sb + h * p.v_sh + (long long)k0 * vss;
   const int nt = (S + BN - 1) / BN;
   const bool ragged = (S % BN) != 0;
   const Ring<TL> ring{smem};
 
-  // Copies of slot 2i: K_{i+1} and V_i.
-  auto copies = [&](int i) {
-    if (i + 1 < nt) {
-      if ((i + 2) * BN <= S)
-        cp.k.issue(kh + (size_t)(i + 1) * BN * D, ring.k(i + 1), wave);
-      else
-        cp.k.issue_clamped(kh, (i + 1) * BN, S, ring.k(i + 1), wave);
-    }
-    if (i < nt) {
-      if ((i + 1) * BN <= S)
-        cp.v.issue(vh + (size_t)i * BN * D, ring.v(i), wave);
-      else
-        cp.v.issue_clamped(vh, i * BN, S, ring.v(i), wave);
-    }
+  // Copy set c(t) = {K_t, V_{t-1}}: the tiles M(t) reads.  Each wave issues its
+  // share; tiles that run past the last key are clamped.
+  auto copy_k = [&](int t) {
+    const uint16_t* kt = kh + (long long)(t * BN) * kss;
+    if ((t + 1) * BN <= S)
+      cp.k.issue(kt, ring.k(t), wave);
+    else
+      cp.k.issue_clamped(kt, S - t * BN, krb, ring.k(t), wave, lane);
+  };
+  auto copy_v = [&](int t) {
+    const uint16_t* vt = vh + (long long)(t * BN) * vss;
+    if ((t + 1) * BN <= S)
+      cp.v.issue(vt, ring.v(t), wave);
+    else
+      cp.v.issue_clamped(vt, S - t * BN, vrb, ring.v(t), wave, lane);
+  };
+  auto copy_set = [&](int t) {
+    if (t < nt) copy_k(t);
+    if (t >= 1 && t <= nt) copy_v(t - 1);
   };
 
-  // Prologue: K_0 in flight while Q is loaded into registers.
-  if (BN <= S)
-    cp.k.issue(kh, ring.k(0), wave);
-  else
-    cp.k.issue_clamped(kh, 0, S, ring.k(0), wave);
+  // Prologue: c(0) and c(1) in flight while Q is loaded into registers.
+  copy_set(0);
+  copy_set(1);
   WaveState<TL> ws;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -584,7 +630,7 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       u32x4_t x = {0u, 0u, 0u, 0u};
-      if (row < S) x = ld_global16(qh + (size_t)row * D + 16 * t + 8 * hh);
+      if (row < p.Sq) x = ld_global16(qh + (long long)row * p.q_ss + 16 * t + 8 * hh);
       ws.qf[qb][t] = x;
     }
     ws.m[qb] = -__builtin_inff();
@@ -597,69 +643,64 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   wait_vmem();
   __syncthreads();
 
+  // Slots: group 0 runs M(i) in slot 2i and V(i) in slot 2i+1, group 1 one
+  // slot later.  In V(i) every wave issues its share of c(i+2); the buffers
+  // it overwrites (K_{i-1}, V_{i-2}) were last read in M(i-1), slots 2i-2 and
+  // 2i-1.  A wave's share of c(i+1) is complete before the barrier that ends
+  // slot 2i+1: group 0 waits at the start of V(i) (issued two slots before),
+  // group 1 at the end of M(i) (issued one slot before).  No DMA is issued or
+  // awaited inside group 0's MFMA phase, and group 1 only awaits copies there.
   SAcc<TL> sacc;
   PFrag<TL> pfr;
-  if (grp == 1) {  // group 1 sits out slot 0
-    copies(0);
-    __syncthreads();
-  }
+  if (grp == 1) __syncthreads();  // group 1 sits out slot 0
   // Step 0: Sᵀ of tile 0, softmax of tile 0.
-  if (grp == 0) copies(0);
   mfma_phase<T, TL, true, false, NEG>(ws, ring.k(0), nullptr, sacc, pfr, lane);
-  if (grp == 1) wait_vmem();
   __syncthreads();
-  if (grp == 1 && nt > 1) copies(1);
+  copy_set(2);
   if (nt == 1 && ragged)
     valu_phase<T, TL, true, NEG>(ws, 0, S, c, thr, sacc, pfr, lane);
   else
     valu_phase<T, TL, false, NEG>(ws, 0, S, c, thr, sacc, pfr, lane);
-  if (grp == 0) wait_vmem();
   __syncthreads();
   // Steps 1 .. nt-1: P·V of tile i-1 and Sᵀ of tile i, softmax of tile i.
-  // Steps 1 .. nt-3 copy only whole tiles and softmax unmasked tiles; the last
-  // two steps are peeled so the steady loop carries no such branches.
-  auto step = [&](int i) {
-    if (grp == 0) copies(i);
+  // Steps 1 .. nt-4 copy only whole tiles and softmax unmasked tiles; the last
+  // three steps are peeled so the steady loop carries no such branches.
+  // One step; `cset` issues the step's copies (c(i+2)), `masked` selects the
+  // softmax of a ragged last tile.
+  auto step = [&](int i, auto cset, auto masked) {
     mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
     if (grp == 1) wait_vmem();
     __syncthreads();
-    if (grp == 1) copies(i + 1);
-    if (i == nt - 1 && ragged)
+    if (grp == 0) wait_vmem();
+    cset();
+    if (masked)
       valu_phase<T, TL, true, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
     else
       valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
-    if (grp == 0) wait_vmem();
     __syncthreads();
   };
-  for (int i = 1; i <= nt - 3; ++i) {
-    if (grp == 0) {
-      cp.k.issue(kh + (size_t)(i + 1) * BN * D, ring.k(i + 1), wave);
-      cp.v.issue(vh + (size_t)i * BN * D, ring.v(i), wave);
-    }
+  for (int i = 1; i <= nt - 4; ++i) {
     mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
     if (grp == 1) wait_vmem();
     __syncthreads();
-    if (grp == 1) {
-      if (i + 2 < nt) {
-        if ((i + 3) * BN <= S)
-          cp.k.issue(kh + (size_t)(i + 2) * BN * D, ring.k(i + 2), wave);
-        else
-          cp.k.issue_clamped(kh, (i + 2) * BN, S, ring.k(i + 2), wave);
-      }
-      cp.v.issue(vh + (size_t)(i + 1) * BN * D, ring.v(i + 1), wave);
-    }
-    valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
     if (grp == 0) wait_vmem();
+    cp.k.issue(kh + (long long)((i + 2) * BN) * kss, ring.k(i + 2), wave);
+    cp.v.issue(vh + (long long)((i + 1) * BN) * vss, ring.v(i + 1), wave);
+    valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
     __syncthreads();
   }
-  if (nt >= 3) step(nt - 2);
-  if (nt >= 2) step(nt - 1);
+  // The last three steps: c(nt-1) = {K_nt-1 (maybe partial), V_nt-2}, then
+  // c(nt) = {V_nt-1 (maybe partial)}, then nothing.
+  if (nt >= 4) step(nt - 3, [&]() { copy_k(nt - 1); copy_v(nt - 2); }, false);
+  if (nt >= 3) step(nt - 2, [&]() { copy_v(nt - 1); }, false);
+  if (nt >= 2) step(nt - 1, []() {}, ragged);
   // Step nt: P·V of the last tile.
   mfma_phase<T, TL, false, true, NEG>(ws, nullptr, ring.v(nt - 1), sacc, pfr, lane);
   if (grp == 0) __syncthreads();  // group 1 has one barrier fewer to go
   __syncthreads();
 
-  store_output<T, TL>(p, ws, head, bh, qt, wave, lane);
+  store_output<T, TL>(p, ws, sp * p.o_split + b * p.o_sb + h * p.o_sh,
+                     sp * p.lse_split + (long long)bh * p.Sq, qt, wave, lane);
 }
 
 
@@ -672,8 +713,8 @@ void attn_fwd_kernel(Params p) {
   const int lane = threadIdx.x & 63;
   const int G = gridDim.x;
   Copies<TL> cp;
-  cp.k.init(wave, lane);
-  cp.v.init(wave, lane);
+  cp.k.init(wave, lane, (uint32_t)p.k_ss * 2u);
+  cp.v.init(wave, lane, (uint32_t)p.v_ss * 2u);
   // Persistent loop over work items ("B200 Attention Kernel from Scratch to
   // Near-SOTA in 60 Diagrams", Chapter 14 - Persistent: a static grid-stride
   // assignment).  Workgroups are dispatched round-robin over the 8 XCDs, so

@@ -34,6 +34,9 @@
 #ifndef DENSE_ATTENTION_AMD_ATTN_H
 #define DENSE_ATTENTION_AMD_ATTN_H
 
+#include <stddef.h>
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -41,7 +44,8 @@ extern "C" {
 /* Element type of q, k, v and o. */
 enum attn_dtype {
   ATTN_F16 = 0,  /* IEEE binary16 */
-  ATTN_BF16 = 1  /* bfloat16 */
+  ATTN_BF16 = 1, /* bfloat16 */
+  ATTN_F32 = 2   /* IEEE binary32: only as the output type of attn_merge */
 };
 
 /* Return codes. */
@@ -125,6 +129,108 @@ int attn_get_config(int B, int H, int S, int D, int dtype,
 int attn_variant_count(void);
 int attn_variant_info(int index, int* id, int* head_dim, int* dtype, int* block_m,
                       int* block_n, int* waves, int* stages);
+
+/* ---- general layouts, KV ranges and split-KV --------------------------------- */
+
+/* Element strides of a [B, H, S, D] view whose head dimension is contiguous
+ * (stride 1).  Contiguous BHSD is {H·S·D, S·D, D}; contiguous BSHD (tokens
+ * outermost, heads interleaved per token) is {S·H·D, D, H·D}.  A slice of keys
+ * [a, b) of a BHSD tensor is the same strides with the base pointer advanced by
+ * a·D.  Every stride must be >= 0 and a multiple of 8 elements (16 bytes), and
+ * seq_stride < 2^24. */
+typedef struct attn_layout {
+  int64_t batch_stride;
+  int64_t head_stride;
+  int64_t seq_stride;
+} attn_layout_t;
+
+/*
+ * attn_fwd_strided — attn_fwd over arbitrary strided views and separate query
+ * and key lengths: o[b,h,i,:] = Σ_j softmax_j(scale·q_i·k_j)·v_j over the Skv
+ * keys of head (b, h), for each of its Sq queries (B200 page, Appendix,
+ * "Benchmark Calibration": a variant that consumes and produces contiguous
+ * BSHD directly, with no layout-conversion copies).
+ *
+ *   q_layout, k_layout, v_layout, o_layout  strides of each tensor; NULL means
+ *            contiguous [B, H, S, D] for that tensor (S = Sq for q and o, Skv
+ *            for k and v).  o must not overlap itself or the inputs.
+ *   lse      contiguous [B, H, Sq] fp32, or NULL.
+ *   Sq, Skv  >= 0; Sq·Skv == 0 with B·H > 0 and Sq > 0 is rejected (a query
+ *            with no keys has no softmax); B·H·Sq == 0 is an empty problem.
+ * Other arguments and errors as attn_fwd_ex.
+ */
+int attn_fwd_strided(const void* q, const attn_layout_t* q_layout,
+                     const void* k, const attn_layout_t* k_layout,
+                     const void* v, const attn_layout_t* v_layout,
+                     void* o, const attn_layout_t* o_layout, float* lse,
+                     int B, int H, int Sq, int Skv, int D, float scale, int dtype, void* stream,
+                     const attn_fwd_options_t* opts);
+
+/*
+ * attn_fwd_partial — attention of Sq queries over one range of Skv keys (for
+ * example one device's shard of the sequence), as the carrier the ranges
+ * merge with ("Learning FlashAttention the Hard Way - Part 2", "Wrap-Up": the
+ * running (max, sum, output) triple is associative, which is what licenses
+ * streaming or splitting the KV axis; its references name split-KV):
+ *
+ *   o_part[b,h,i,:]  = Σ_{j in range} e^{s_ij - lse_part[b,h,i]} v_j   (fp32)
+ *   lse_part[b,h,i]  = ln Σ_{j in range} e^{s_ij},   s_ij = scale·q_i·k_j
+ *
+ *   o_part    device pointer, contiguous [B, H, Sq, D] fp32, 16-byte aligned.
+ *   lse_part  device pointer, contiguous [B, H, Sq] fp32; required.
+ * Inputs, layouts and errors as attn_fwd_strided; Skv >= 1.
+ */
+int attn_fwd_partial(const void* q, const attn_layout_t* q_layout,
+                     const void* k, const attn_layout_t* k_layout,
+                     const void* v, const attn_layout_t* v_layout,
+                     float* o_part, float* lse_part,
+                     int B, int H, int Sq, int Skv, int D, float scale, int dtype, void* stream,
+                     const attn_fwd_options_t* opts);
+
+/*
+ * attn_merge — combines n_parts partials of disjoint key ranges of the same
+ * queries into the attention over their union:
+ *
+ *   lse = ln Σ_g e^{lse_g},   o = Σ_g e^{lse_g - lse} · o_g
+ *
+ * (the combine step of the same page's "The Move Stack": partial reductions
+ * of separate workgroups joined by a separate kernel).
+ *
+ *   o_parts    n_parts consecutive contiguous [B, H, S, D] fp32 arrays.
+ *   lse_parts  n_parts consecutive contiguous [B, H, S] fp32 arrays.  A
+ *              partial with lse = -inf (no keys) has weight 0; a row whose
+ *              partials are all -inf gets o = 0 and lse = -inf.
+ *   o          output of `dtype` (ATTN_F16, ATTN_BF16, or ATTN_F32 for an
+ *              fp32 result that can itself be merged again), strides o_layout
+ *              (NULL = contiguous), 16-byte aligned.
+ *   lse        contiguous [B, H, S] fp32, or NULL.
+ *   n_parts    >= 1.
+ */
+int attn_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o,
+               const attn_layout_t* o_layout, float* lse, int B, int H, int S, int D, int dtype,
+               void* stream);
+
+/*
+ * attn_fwd_split — attn_fwd with the keys of every (b, h, query tile) split
+ * into `kv_splits` ranges processed by separate workgroups, then merged: more
+ * independent work items when B·H·ceil(S/block_m) would leave compute units
+ * idle.  One launch computes all partials into `workspace`, a second merges
+ * them into o and lse.
+ *
+ *   kv_splits        >= 1, or 0 for the library's choice (enough items to
+ *                    fill every compute unit, each range at least 256 keys).
+ *   workspace        device memory of at least
+ *                    attn_fwd_split_workspace_size(B, H, S, D, kv_splits)
+ *                    bytes, 256-byte aligned, owned by the caller; its
+ *                    contents on entry do not matter and on return are
+ *                    unspecified.  Calls that share a workspace must be
+ *                    ordered on one stream.
+ * Other arguments as attn_fwd_ex.
+ */
+size_t attn_fwd_split_workspace_size(int B, int H, int S, int D, int kv_splits);
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int S, int D, float scale, int dtype, void* stream, int kv_splits,
+                   void* workspace, size_t workspace_bytes, const attn_fwd_options_t* opts);
 
 /* Static description of a status code.  Never NULL. */
 const char* attn_strerror(int status);

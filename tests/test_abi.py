@@ -67,7 +67,7 @@ def test_rejects_bad_shapes(lib):
     assert _call(lib, B=-2) == -3
     assert _call(lib, D=96) == -3
     assert _call(lib, D=0) == -3
-    assert _call(lib, S=1 << 24, D=128) == -3          # S*D overflows 31 bits
+    assert _call(lib, S=1 << 30, D=128) == -3          # key index beyond 2^30
     assert _call(lib, B=1 << 12, H=1 << 12, S=1 << 8) == -3
 
 
@@ -155,3 +155,75 @@ def test_binding_validates_before_calling(lib):
     with pytest.raises(TypeError):
         da._dtype_code(torch.zeros(1, dtype=torch.float32))
     assert math.isclose(1.0 / math.sqrt(64), 0.125)
+
+
+# --- strided, partial, merge and split entry points: validation without a device ----
+
+FAKE = 1 << 20   # a 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def _layout(b, h, s):
+    return da.attn_layout(b, h, s)
+
+
+def test_strided_rejects_bad_layouts(lib):
+    B, H, S, D = 1, 2, 64, 64
+    ok = _layout(H * S * D, S * D, D)
+    bad_mult = _layout(H * S * D, S * D, D + 4)        # not a multiple of 8 elements
+    neg = _layout(-8, S * D, D)
+    huge = _layout(H * S * D, S * D, 1 << 24)
+    narrow_o = _layout(H * S * D, S * D, 32)            # output rows would overlap
+    f = ctypes.c_float(0.125)
+    for ql, ol in [(bad_mult, ok), (neg, ok), (huge, ok), (ok, narrow_o)]:
+        st = lib.attn_fwd_strided(FAKE, ctypes.byref(ql), FAKE, ctypes.byref(ok), FAKE,
+                                  ctypes.byref(ok), FAKE, ctypes.byref(ol), None, B, H, S, S, D,
+                                  f, da.ATTN_BF16, None, None)
+        assert st == -3, (ql.seq_stride, ol.seq_stride)
+    # queries without keys have no softmax
+    st = lib.attn_fwd_strided(FAKE, None, FAKE, None, FAKE, None, FAKE, None, None, B, H, S, 0, D,
+                              f, da.ATTN_BF16, None, None)
+    assert st == -3
+    # no queries: empty, fine without pointers
+    st = lib.attn_fwd_strided(None, None, None, None, None, None, None, None, None, B, H, 0, 5, D,
+                              f, da.ATTN_BF16, None, None)
+    assert st == 0
+
+
+def test_partial_requires_lse(lib):
+    st = lib.attn_fwd_partial(FAKE, None, FAKE, None, FAKE, None, FAKE, None, 1, 1, 64, 64, 64,
+                              ctypes.c_float(0.1), da.ATTN_F16, None, None)
+    assert st == -1
+
+
+def test_merge_validation(lib):
+    args = dict(B=1, H=1, S=8, D=64, dtype=da.ATTN_F32)
+
+    def merge(n=2, o_parts=FAKE, lse_parts=FAKE, o=FAKE, **kw):
+        a = dict(args, **kw)
+        return lib.attn_merge(o_parts, lse_parts, n, o, None, None, a["B"], a["H"], a["S"],
+                              a["D"], a["dtype"], None)
+
+    assert merge(n=0) == -8
+    assert merge(dtype=3) == -2
+    assert merge(D=96) == -3
+    assert merge(o=None) == -1
+    assert merge(o_parts=FAKE + 4) == -4
+    assert merge(S=0, o=None, o_parts=None, lse_parts=None) == 0
+
+
+def test_split_validation_and_workspace_size(lib):
+    f = ctypes.c_float(0.1)
+    assert lib.attn_fwd_split(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 512, 64, f, da.ATTN_F16, None,
+                              65, FAKE, 1 << 20, None) == -8
+    assert lib.attn_fwd_split(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 512, 64, f, da.ATTN_F16, None,
+                              -1, FAKE, 1 << 20, None) == -8
+    # partial O (fp32) then partial LSE, each rounded up to 256 bytes
+    n, B, H, S, D = 3, 2, 4, 1000, 128
+    o_bytes = n * B * H * S * D * 4
+    l_bytes = n * B * H * S * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert lib.attn_fwd_split_workspace_size(B, H, S, D, n) == up(o_bytes) + up(l_bytes)
+    # automatic choice: sized for at most S / 256 ranges (capped at 64, at least 1)
+    assert lib.attn_fwd_split_workspace_size(1, 1, 4096, 64, 0) == up(16 * 4096 * 64 * 4) + up(16 * 4096 * 4)
+    assert lib.attn_fwd_split_workspace_size(1, 1, 100, 64, 0) == up(100 * 64 * 4) + up(100 * 4)
+    assert lib.attn_fwd_split_workspace_size(1, 1, 100, 96, 1) == 0
