@@ -126,7 +126,8 @@ struct Tile {
   static constexpr int VS = D * 2 + 64;     // LDS row stride of V (bytes)
   static constexpr int K_TILE = BN * KS;
   static constexpr int V_TILE = BN * VS;
-  static constexpr int STAGES = 3;           // three K and three V buffers
+  // K/V ring depth: three tiles when they fit in LDS, else two.
+  static constexpr int STAGES = 3 * (BN * (KS + VS)) <= 160 * 1024 ? 3 : 2;
   static constexpr int LDS_BYTES = STAGES * (K_TILE + V_TILE);
   // Waves per SIMD the register allocation targets.
   static constexpr int WPE = NW / 4;
@@ -269,8 +270,8 @@ struct WaveState {
 //   PV: Oᵀ += Vᵀ·Pᵀ with the tile in `vl` and P from `p_in`.
 // The stages touch disjoint registers.  The work is laid out as R regions:
 // region r issues QK MFMA r and PV MFMA r together with the LDS reads of
-// their operands two (K) and one (V) regions ahead, so every MFMA finds its
-// operands loaded.  When the softmax runs alone it is issued as wide
+// their operands two regions ahead, so every MFMA finds its operands
+// loaded.  When the softmax runs alone it is issued as wide
 // independent passes (see below); when it runs beside MFMAs its slices are
 // spread over the regions and scheduling barriers keep them there.
 
@@ -311,8 +312,10 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
   const lds_t* kbase = (const lds_t*)(uintptr_t)ka;
   const lds_t* vbase = (const lds_t*)(uintptr_t)va;
 
+  // QK MFMA i works on key block i % NB and head-dim step i / NB, so
+  // consecutive QK MFMAs accumulate into different key blocks.
   auto kfrag = [&](int i) -> u32x4_t {
-    return ld_lds16(kbase + (i / DT) * 32 * TL::KS + (i % DT) * 32);
+    return ld_lds16(kbase + (i % NB) * 32 * TL::KS + (i / NB) * 32);
   };
   auto vfrag = [&](int i) -> u32x4_t {
     const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
@@ -323,13 +326,19 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
     return a;
   };
 
+  // Operands are read KD (K) and VD (V) regions ahead of their MFMA: one
+  // region is one or two MFMAs (32-64 cycles), shorter than an LDS read.
+  constexpr int KD = 2, VD = 2;
   u32x4_t kf[NQ];
   u32x4_t vf[NP];
   if (QK) {
-    kf[0] = kfrag(0);
-    kf[1] = kfrag(1);
+#pragma unroll
+    for (int j = 0; j < KD && j < NQ; ++j) kf[j] = kfrag(j);
   }
-  if (PV) vf[0] = vfrag(0);
+  if (PV) {
+#pragma unroll
+    for (int j = 0; j < VD && j < NP; ++j) vf[j] = vfrag(j);
+  }
 
   // softmax state.  Key kb + 16·hh + 32·nb + i of a tile is valid iff
   // 32·nb + i < lim; lim is opaque so the compares stay inside the step.
@@ -344,11 +353,11 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
   for (int r = 0; r < R; ++r) {
     // ---- MFMA work of region r ----
     if (QK && r < NQ) {
-      const int nb = r / DT, t = r % DT;
+      const int nb = r % NB, t = r / NB;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         s_out[qb][nb] = Mma<T>::mfma(kf[r], ws.qf[qb][t], t == 0 ? zero : s_out[qb][nb]);
-      if (r + 2 < NQ) kf[r + 2] = kfrag(r + 2);
+      if (r + KD < NQ) kf[r + KD] = kfrag(r + KD);
     }
     if (PV && r < NP) {
       const int nb = r / (2 * DB), mm = (r / DB) % 2, db = r % DB;
@@ -358,7 +367,7 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
                            p_in[qb][nb][4 * mm + 2], p_in[qb][nb][4 * mm + 3]};
         ws.o[qb][db] = Mma<T>::mfma(vf[r], b, ws.o[qb][db]);
       }
-      if (r + 1 < NP) vf[r + 1] = vfrag(r + 1);
+      if (r + VD < NP) vf[r + VD] = vfrag(r + VD);
     }
     // ---- softmax slice of region r ----
     if (SM) {
@@ -463,14 +472,14 @@ __device__ __forceinline__ void rescale_o(WaveState<TL>& ws, const float (&alpha
       for (int i = 0; i < 16; ++i) ws.o[qb][db][i] *= alpha[qb];
 }
 
-// LDS ring: three K buffers then three V buffers; K_t lives in K buffer t%3
-// and V_t in V buffer t%3.
+// LDS ring: STAGES K buffers then STAGES V buffers; K_t lives in K buffer
+// t % STAGES and V_t in V buffer t % STAGES.
 template <class TL>
 struct Ring {
   lds_t* base;
-  __device__ __forceinline__ lds_t* k(int t) const { return base + (t % 3) * TL::K_TILE; }
+  __device__ __forceinline__ lds_t* k(int t) const { return base + (t % TL::STAGES) * TL::K_TILE; }
   __device__ __forceinline__ lds_t* v(int t) const {
-    return base + 3 * TL::K_TILE + (t % 3) * TL::V_TILE;
+    return base + TL::STAGES * TL::K_TILE + (t % TL::STAGES) * TL::V_TILE;
   }
 };
 
@@ -620,9 +629,11 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     if (t >= 1 && t <= nt) copy_v(t - 1);
   };
 
-  // Prologue: c(0) and c(1) in flight while Q is loaded into registers.
+  // Prologue: c(0) (and with a three-deep ring c(1)) in flight while Q is
+  // loaded into registers.
+  constexpr bool DEEP = TL::STAGES == 3;
   copy_set(0);
-  copy_set(1);
+  if (DEEP) copy_set(1);
   WaveState<TL> ws;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -644,56 +655,62 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   __syncthreads();
 
   // Slots: group 0 runs M(i) in slot 2i and V(i) in slot 2i+1, group 1 one
-  // slot later.  In V(i) every wave issues its share of c(i+2); the buffers
-  // it overwrites (K_{i-1}, V_{i-2}) were last read in M(i-1), slots 2i-2 and
-  // 2i-1.  A wave's share of c(i+1) is complete before the barrier that ends
-  // slot 2i+1: group 0 waits at the start of V(i) (issued two slots before),
-  // group 1 at the end of M(i) (issued one slot before).  No DMA is issued or
-  // awaited inside group 0's MFMA phase, and group 1 only awaits copies there.
+  // slot later.  Copies are issued only in V phases: in V(i) a wave issues its
+  // share of c(i + ahead).  A wave's share of c(i+1) is complete before the
+  // barrier that ends slot 2i+1 (M(i+1) of group 0 reads it in slot 2i+2):
+  // group 1 waits at the end of M(i), group 0 in V(i).
+  //  * three-deep ring: ahead = 2 for both groups; group 0 waits at the start
+  //    of V(i).  c(i+2) overwrites K_{i-1} and V_{i-2}, last read in M(i-1)
+  //    (slots 2i-2 and 2i-1).
+  //  * two-deep ring: ahead = 1 for group 0, which waits at the end of V(i)
+  //    (after its softmax), and 2 for group 1.  c(i+1) issued in slot 2i+1
+  //    overwrites K_{i-1} and V_{i-2} (read in slots 2i-2, 2i-1); c(i+2)
+  //    issued by group 1 in slot 2i+2 overwrites K_i and V_{i-1} (read in
+  //    slots 2i, 2i+1).
+  // No DMA is issued or awaited inside group 0's MFMA phase.
+  const int ahead = (DEEP || grp == 1) ? 2 : 1;
   SAcc<TL> sacc;
   PFrag<TL> pfr;
-  if (grp == 1) __syncthreads();  // group 1 sits out slot 0
-  // Step 0: Sᵀ of tile 0, softmax of tile 0.
-  mfma_phase<T, TL, true, false, NEG>(ws, ring.k(0), nullptr, sacc, pfr, lane);
-  __syncthreads();
-  copy_set(2);
-  if (nt == 1 && ragged)
-    valu_phase<T, TL, true, NEG>(ws, 0, S, c, thr, sacc, pfr, lane);
-  else
-    valu_phase<T, TL, false, NEG>(ws, 0, S, c, thr, sacc, pfr, lane);
-  __syncthreads();
-  // Steps 1 .. nt-1: P·V of tile i-1 and Sᵀ of tile i, softmax of tile i.
-  // Steps 1 .. nt-4 copy only whole tiles and softmax unmasked tiles; the last
-  // three steps are peeled so the steady loop carries no such branches.
-  // One step; `cset` issues the step's copies (c(i+2)), `masked` selects the
-  // softmax of a ragged last tile.
-  auto step = [&](int i, auto cset, auto masked) {
-    mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
+  if (grp == 1) {  // group 1 sits out slot 0
+    if (!DEEP) copy_set(1);
+    __syncthreads();
+  }
+  // One step i: M(i) (P·V of tile i-1 unless i == 0, Sᵀ of tile i), then V(i)
+  // (softmax of tile i, masked when it is a ragged last tile).  `cset`
+  // issues the step's copies.
+  auto step = [&](int i, auto cset, bool masked) {
+    if (i == 0)
+      mfma_phase<T, TL, true, false, NEG>(ws, ring.k(0), nullptr, sacc, pfr, lane);
+    else
+      mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
     if (grp == 1) wait_vmem();
     __syncthreads();
-    if (grp == 0) wait_vmem();
+    if (DEEP && grp == 0) wait_vmem();
     cset();
     if (masked)
       valu_phase<T, TL, true, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
     else
       valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
+    if (!DEEP && grp == 0) wait_vmem();
     __syncthreads();
   };
+  step(0, [&]() { copy_set(ahead); }, nt == 1 && ragged);
+  // Steps 1 .. nt-4 copy only whole tiles and softmax unmasked tiles; the last
+  // three steps are peeled so the steady loop carries no such branches.
   for (int i = 1; i <= nt - 4; ++i) {
     mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
     if (grp == 1) wait_vmem();
     __syncthreads();
-    if (grp == 0) wait_vmem();
-    cp.k.issue(kh + (long long)((i + 2) * BN) * kss, ring.k(i + 2), wave);
-    cp.v.issue(vh + (long long)((i + 1) * BN) * vss, ring.v(i + 1), wave);
+    if (DEEP && grp == 0) wait_vmem();
+    const int j = i + ahead;
+    cp.k.issue(kh + (long long)(j * BN) * kss, ring.k(j), wave);
+    cp.v.issue(vh + (long long)((j - 1) * BN) * vss, ring.v(j - 1), wave);
     valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
+    if (!DEEP && grp == 0) wait_vmem();
     __syncthreads();
   }
-  // The last three steps: c(nt-1) = {K_nt-1 (maybe partial), V_nt-2}, then
-  // c(nt) = {V_nt-1 (maybe partial)}, then nothing.
-  if (nt >= 4) step(nt - 3, [&]() { copy_k(nt - 1); copy_v(nt - 2); }, false);
-  if (nt >= 3) step(nt - 2, [&]() { copy_v(nt - 1); }, false);
-  if (nt >= 2) step(nt - 1, []() {}, ragged);
+  for (int i = nt - 3 > 1 ? nt - 3 : 1; i < nt; ++i)
+    step(i, [&]() { copy_set(i + ahead); }, i == nt - 1 && ragged);
   // Step nt: P·V of the last tile.
   mfma_phase<T, TL, false, true, NEG>(ws, nullptr, ring.v(nt - 1), sacc, pfr, lane);
   if (grp == 0) __syncthreads();  // group 1 has one barrier fewer to go
