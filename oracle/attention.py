@@ -14,6 +14,9 @@ directly, materialising every full row of the score matrix:
     o_id   = (sum_j e_ij v_jd) / l_i                      (normalised output)
     lse_i  = m_i + ln l_i                                 (natural-log log-sum-exp)
 
+With a causal mask the maximum, the sums and the log-sum-exp run over the
+keys j <= i + offset only; a row that sees no key has o = 0 and lse = -inf.
+
 Sources.  The per-(batch, head, query-tile) work split, the S = Q·Kᵀ / softmax
 / P·V sections and the final division by the row sum follow "B200 Attention
 Kernel from Scratch to Near-SOTA in 60 Diagrams", Chapter 1, "ii. Work
@@ -44,21 +47,39 @@ def _as_f64(x) -> np.ndarray:
     return a
 
 
-def _rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float):
-    """Attention of the query rows ``qh`` [R, D] against one head's keys/values [Skv, D]."""
-    s = scale * (qh @ kh.T)                 # [R, S] scores
+def _rows(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, mask=None):
+    """Attention of the query rows ``qh`` [R, D] against one head's keys/values [Skv, D].
+
+    ``mask`` (optional, bool [R, Skv]) marks the keys each row may attend to;
+    a row with no such key gets o = 0 and lse = -inf.
+    """
+    s = scale * (qh @ kh.T)                 # [R, Skv] scores
+    if mask is not None:
+        s = np.where(mask, s, -np.inf)
     m = s.max(axis=1, keepdims=True)        # [R, 1] row maxima
-    e = np.exp(s - m)                       # [R, S]
+    seen = np.isfinite(m[:, 0])             # rows with at least one key
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe)                  # [R, Skv]; masked scores give 0
     l = e.sum(axis=1, keepdims=True)        # [R, 1] row sums
-    o = (e @ vh) / l                        # [R, D]
-    lse = m[:, 0] + np.log(l[:, 0])         # [R]
+    o = (e @ vh) / np.where(seen[:, None], l, 1.0)      # [R, D]
+    lse = np.where(seen, m_safe[:, 0] + np.log(np.where(seen, l[:, 0], 1.0)), -np.inf)
     return o, lse
 
 
-def attention_forward(q, k, v, scale: float, row_block: int = 1024):
+def causal_mask(rows, Skv: int, offset: int):
+    """Keys visible to query rows ``rows`` under a causal mask: key j is
+    visible to query row i iff j <= i + offset (offset = Skv - Sq aligns the
+    last query row with the last key)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return np.arange(Skv)[None, :] <= rows[:, None] + offset
+
+
+def attention_forward(q, k, v, scale: float, row_block: int = 1024, causal_offset=None):
     """Full forward.  q is [B, H, Sq, D]; k and v are [B, H, Skv, D] (Skv >= 1; the
-    usual self-attention case has Skv = Sq).  Every query row attends to all Skv
-    keys of its head.  Returns (o [B,H,Sq,D], lse [B,H,Sq]) in float64."""
+    usual self-attention case has Skv = Sq).  Without a mask every query row
+    attends to all Skv keys of its head; with ``causal_offset`` (an int) query
+    row i attends to keys j <= i + causal_offset.  Returns (o [B,H,Sq,D],
+    lse [B,H,Sq]) in float64."""
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, H, S, D = q.shape
     Skv = k.shape[2]
@@ -70,12 +91,14 @@ def attention_forward(q, k, v, scale: float, row_block: int = 1024):
         for h in range(H):
             for r0 in range(0, S, row_block):
                 r1 = min(S, r0 + row_block)
-                o[b, h, r0:r1], lse[b, h, r0:r1] = _rows(q[b, h, r0:r1], k[b, h], v[b, h], scale)
+                mask = None if causal_offset is None else causal_mask(range(r0, r1), Skv, causal_offset)
+                o[b, h, r0:r1], lse[b, h, r0:r1] = _rows(q[b, h, r0:r1], k[b, h], v[b, h], scale, mask)
     return o, lse
 
 
-def attention_rows(q, k, v, scale: float, b: int, h: int, rows):
-    """The same definition for selected query rows of one (b, h) only, each against all keys.
+def attention_rows(q, k, v, scale: float, b: int, h: int, rows, causal_offset=None):
+    """The same definition for selected query rows of one (b, h) only, each against all keys
+    (or the keys the causal mask lets it see).
 
     Used to check large problems on a sample of output rows.  Returns
     (o [len(rows), D], lse [len(rows)]) in float64.
@@ -84,4 +107,5 @@ def attention_rows(q, k, v, scale: float, b: int, h: int, rows):
     qh = np.asarray(q[b, h], dtype=np.float64)[rows]
     kh = np.asarray(k[b, h], dtype=np.float64)
     vh = np.asarray(v[b, h], dtype=np.float64)
-    return _rows(qh, kh, vh, scale)
+    mask = None if causal_offset is None else causal_mask(rows, kh.shape[0], causal_offset)
+    return _rows(qh, kh, vh, scale, mask)

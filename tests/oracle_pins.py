@@ -11,7 +11,11 @@ mathematics fixed independently of the oracle's own code:
   float64 on the CPU, and ``scipy.special.logsumexp`` for the LSE;
 * closed forms (zero query, zero scale, constant V, a single key, two keys,
   one dominant key at huge logits) and invariants (per-row logit shift, joint
-  permutation of keys and values, permutation of queries, convex hull).
+  permutation of keys and values, permutation of queries, convex hull);
+* for the causal mask: the brute force over the visible keys only, torch's
+  is_causal (equal lengths) or an explicit lower-triangular boolean mask
+  (other lengths), the first row (one key) and the last row (all keys), and
+  rows that see no key.
 
 The same pins are run against planted mistakes in ``test_oracle.py`` to show
 that each plausible slip fails at least one of them.
@@ -241,7 +245,112 @@ def pin_convex_hull(fwd):
     assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12)
 
 
+# --- causal mask: key j is visible to query row i iff j <= i + offset -----------------
+
+def _brute_causal(q, k, v, scale, offset):
+    """Independent arrangement over the visible keys only; a row without any
+    visible key is defined as o = 0, lse = -inf."""
+    B, H, S, D = q.shape
+    Skv = k.shape[2]
+    o = np.zeros((B, H, S, D))
+    lse = np.full((B, H, S), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            for i in range(S):
+                vis = [j for j in range(Skv) if j - i <= offset]
+                if not vis:
+                    continue
+                s = {j: scale * math.fsum(q[b, h, i, d] * k[b, h, j, d] for d in range(D)) for j in vis}
+                for t in vis:
+                    w = 1.0 / math.fsum(math.exp(s[j] - s[t]) for j in vis)
+                    for d in range(D):
+                        o[b, h, i, d] += w * v[b, h, t, d]
+                lse[b, h, i] = math.log(math.fsum(math.exp(x) for x in s.values()))
+    return o, lse
+
+
+def pin_causal_brute_force(fwd):
+    rng = _rng(4321)
+    for (B, H, Sq, Skv, D, scale, off) in [(1, 1, 5, 5, 3, 1.0, 0), (2, 1, 7, 7, 2, 0.5, 0),
+                                           (1, 2, 3, 8, 4, 0.7, 5), (1, 1, 8, 3, 2, 1.0, -5),
+                                           (1, 1, 6, 6, 3, 0.9, 2), (1, 1, 6, 6, 3, 0.9, -2)]:
+        q = rng.integers(-3, 4, size=(B, H, Sq, D)).astype(np.float64)
+        k = rng.integers(-3, 4, size=(B, H, Skv, D)).astype(np.float64)
+        v = rng.normal(size=(B, H, Skv, D))
+        o, lse = fwd(q, k, v, scale, causal_offset=off)
+        bo, bl = _brute_causal(q, k, v, scale, off)
+        np.testing.assert_allclose(np.asarray(o), bo, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(np.isneginf(np.asarray(lse)), np.isneginf(bl))
+        fin = np.isfinite(bl)
+        np.testing.assert_allclose(np.asarray(lse)[fin], bl[fin], rtol=0, atol=1e-12)
+
+
+def pin_causal_torch_sdpa(fwd):
+    """Equal lengths: torch's is_causal.  Other lengths: the boolean mask
+    tril(diagonal = Skv - Sq), i.e. the last query row sees every key."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = _rng(77)
+    for (B, H, Sq, Skv, D) in [(1, 2, 128, 128, 64), (2, 1, 100, 100, 32), (1, 2, 37, 211, 64),
+                               (1, 1, 200, 200, 16)]:
+        q = rng.standard_normal((B, H, Sq, D))
+        k = rng.standard_normal((B, H, Skv, D))
+        v = rng.standard_normal((B, H, Skv, D))
+        scale = 1.0 / math.sqrt(D)
+        o, lse = fwd(q, k, v, scale, causal_offset=Skv - Sq)
+        tq, tk, tv = torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)
+        if Sq == Skv:
+            ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale).numpy()
+        else:
+            m = torch.ones(Sq, Skv, dtype=torch.bool).tril(diagonal=Skv - Sq)
+            ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale).numpy()
+        np.testing.assert_allclose(np.asarray(o), ref, rtol=0, atol=1e-12)
+        scores = scale * np.einsum("bhid,bhjd->bhij", q, k)
+        vis = np.arange(Skv)[None, :] <= np.arange(Sq)[:, None] + (Skv - Sq)
+        mx = np.where(vis, scores, -np.inf).max(axis=-1)
+        ref_l = mx + np.log(np.where(vis, np.exp(scores - mx[..., None]), 0.0).sum(axis=-1))
+        np.testing.assert_allclose(np.asarray(lse), ref_l, rtol=0, atol=1e-12)
+
+
+def pin_causal_first_and_last_rows(fwd):
+    """Equal lengths: row 0 sees key 0 only (o = v_0, lse = scale q_0·k_0);
+    the last row sees every key, as in torch's unmasked attention."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = _rng(78)
+    q = rng.standard_normal((2, 2, 50, 8))
+    k = rng.standard_normal((2, 2, 50, 8))
+    v = rng.standard_normal((2, 2, 50, 8))
+    o, lse = fwd(q, k, v, 0.4, causal_offset=0)
+    np.testing.assert_allclose(np.asarray(o)[:, :, 0], v[:, :, 0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(np.asarray(lse)[:, :, 0], 0.4 * (q[:, :, 0] * k[:, :, 0]).sum(-1),
+                               rtol=0, atol=1e-13)
+    full = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                          torch.from_numpy(v), scale=0.4).numpy()
+    np.testing.assert_allclose(np.asarray(o)[:, :, -1], full[:, :, -1], rtol=0, atol=1e-12)
+
+
+def pin_causal_rows_without_keys(fwd):
+    """More queries than keys, last rows aligned: the first Sq - Skv rows see
+    nothing (o = 0, lse = -inf); row Sq - Skv sees key 0 only."""
+    rng = _rng(79)
+    q = rng.standard_normal((1, 1, 9, 4))
+    k = rng.standard_normal((1, 1, 4, 4))
+    v = rng.standard_normal((1, 1, 4, 4))
+    o, lse = fwd(q, k, v, 0.5, causal_offset=4 - 9)
+    o, lse = np.asarray(o), np.asarray(lse)
+    assert np.all(o[0, 0, :5] == 0.0) and np.all(np.isneginf(lse[0, 0, :5]))
+    np.testing.assert_allclose(o[0, 0, 5], v[0, 0, 0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0, 5], 0.5 * q[0, 0, 5] @ k[0, 0, 0], rtol=0, atol=1e-13)
+
+
 ALL_PINS = [
+    pin_causal_brute_force,
+    pin_causal_torch_sdpa,
+    pin_causal_first_and_last_rows,
+    pin_causal_rows_without_keys,
     pin_golden_fractions,
     pin_brute_force_tiny,
     pin_torch_sdpa,

@@ -49,7 +49,7 @@ def test_rejects_mismatched_shapes():
 
 # --- planted mistakes -------------------------------------------------------
 
-def _m_transposed_scores(qh, kh, vh, scale):
+def _m_transposed_scores(qh, kh, vh, scale, mask=None):
     s = scale * (kh @ qh.T)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -57,15 +57,15 @@ def _m_transposed_scores(qh, kh, vh, scale):
     return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
 
 
-def _m_no_scale(qh, kh, vh, scale):
-    return oa.__dict__["_orig_rows"](qh, kh, vh, 1.0)
+def _m_no_scale(qh, kh, vh, scale, mask=None):
+    return oa.__dict__["_orig_rows"](qh, kh, vh, 1.0, mask)
 
 
-def _m_sign(qh, kh, vh, scale):
-    return oa.__dict__["_orig_rows"](qh, kh, vh, -scale)
+def _m_sign(qh, kh, vh, scale, mask=None):
+    return oa.__dict__["_orig_rows"](qh, kh, vh, -scale, mask)
 
 
-def _m_wrong_axis(qh, kh, vh, scale):
+def _m_wrong_axis(qh, kh, vh, scale, mask=None):
     s = scale * (qh @ kh.T)
     m = s.max(axis=0, keepdims=True)
     e = np.exp(s - m)
@@ -74,25 +74,25 @@ def _m_wrong_axis(qh, kh, vh, scale):
     return o, np.log(np.exp(s).sum(axis=1))
 
 
-def _m_no_max_subtraction(qh, kh, vh, scale):
+def _m_no_max_subtraction(qh, kh, vh, scale, mask=None):
     s = scale * (qh @ kh.T)
     e = np.exp(s)
     l = e.sum(axis=1, keepdims=True)
     return (e @ vh) / l, np.log(l[:, 0])
 
 
-def _m_lse_without_max(qh, kh, vh, scale):
-    o, lse = oa.__dict__["_orig_rows"](qh, kh, vh, scale)
+def _m_lse_without_max(qh, kh, vh, scale, mask=None):
+    o, lse = oa.__dict__["_orig_rows"](qh, kh, vh, scale, mask)
     m = (scale * (qh @ kh.T)).max(axis=1)
     return o, lse - m
 
 
-def _m_lse_base2(qh, kh, vh, scale):
-    o, lse = oa.__dict__["_orig_rows"](qh, kh, vh, scale)
+def _m_lse_base2(qh, kh, vh, scale, mask=None):
+    o, lse = oa.__dict__["_orig_rows"](qh, kh, vh, scale, mask)
     return o, lse / np.log(2.0)
 
 
-def _m_no_normalisation(qh, kh, vh, scale):
+def _m_no_normalisation(qh, kh, vh, scale, mask=None):
     s = scale * (qh @ kh.T)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -100,7 +100,7 @@ def _m_no_normalisation(qh, kh, vh, scale):
     return e @ vh, m[:, 0] + np.log(l[:, 0])
 
 
-def _m_dropped_last_key_in_sum(qh, kh, vh, scale):
+def _m_dropped_last_key_in_sum(qh, kh, vh, scale, mask=None):
     s = scale * (qh @ kh.T)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -108,15 +108,15 @@ def _m_dropped_last_key_in_sum(qh, kh, vh, scale):
     return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
 
 
-def _m_reversed_values(qh, kh, vh, scale):
-    return oa.__dict__["_orig_rows"](qh, kh, vh[::-1], scale)
+def _m_reversed_values(qh, kh, vh, scale, mask=None):
+    return oa.__dict__["_orig_rows"](qh, kh, vh[::-1], scale, mask)
 
 
-def _m_keys_used_as_values(qh, kh, vh, scale):
-    return oa.__dict__["_orig_rows"](qh, kh, kh, scale)
+def _m_keys_used_as_values(qh, kh, vh, scale, mask=None):
+    return oa.__dict__["_orig_rows"](qh, kh, kh, scale, mask)
 
 
-def _m_off_by_one_key(qh, kh, vh, scale):
+def _m_off_by_one_key(qh, kh, vh, scale, mask=None):
     s = scale * (qh @ np.roll(kh, 1, axis=0).T)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -124,7 +124,7 @@ def _m_off_by_one_key(qh, kh, vh, scale):
     return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
 
 
-def _m_exp2_instead_of_exp(qh, kh, vh, scale):
+def _m_exp2_instead_of_exp(qh, kh, vh, scale, mask=None):
     s = scale * (qh @ kh.T)
     m = s.max(axis=1, keepdims=True)
     e = np.exp2(s - m)
@@ -141,6 +141,43 @@ MUTANTS = [_m_transposed_scores, _m_no_scale, _m_sign, _m_wrong_axis, _m_no_max_
 def test_planted_mistake_fails_some_pin(mutant, monkeypatch):
     monkeypatch.setitem(oa.__dict__, "_orig_rows", oa._rows)
     monkeypatch.setattr(oa, "_rows", mutant)
+    failed = []
+    with np.errstate(all="ignore"):
+        for pin in P.ALL_PINS:
+            try:
+                pin(oa.attention_forward)
+            except (AssertionError, ValueError, FloatingPointError):
+                failed.append(pin.__name__)
+    assert failed, f"planted mistake {mutant.__name__} passed every pin"
+
+
+# --- planted mistakes in the causal mask ---------------------------------------------
+
+def _c_strict(rows, Skv, offset):          # j < i + offset: the diagonal key dropped
+    rows = np.asarray(rows)
+    return np.arange(Skv)[None, :] < rows[:, None] + offset
+
+
+def _c_top_left(rows, Skv, offset):        # alignment ignored: j <= i
+    rows = np.asarray(rows)
+    return np.arange(Skv)[None, :] <= rows[:, None]
+
+
+def _c_transposed(rows, Skv, offset):      # j >= i + offset
+    rows = np.asarray(rows)
+    return np.arange(Skv)[None, :] >= rows[:, None] + offset
+
+
+def _c_none(rows, Skv, offset):            # mask ignored
+    return np.ones((len(np.asarray(rows)), Skv), dtype=bool)
+
+
+CAUSAL_MUTANTS = [_c_strict, _c_top_left, _c_transposed, _c_none]
+
+
+@pytest.mark.parametrize("mutant", CAUSAL_MUTANTS, ids=lambda f: f.__name__)
+def test_planted_causal_mistake_fails_some_pin(mutant, monkeypatch):
+    monkeypatch.setattr(oa, "causal_mask", mutant)
     failed = []
     with np.errstate(all="ignore"):
         for pin in P.ALL_PINS:
