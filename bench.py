@@ -56,7 +56,7 @@ def measured_traffic(workload: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, seconds: float):
+def cpu_baseline(w, q, k, v, seconds: float, causal: bool = False):
     """Times the float64 oracle on whole heads of the workload for about `seconds`.
 
     Heads (b, h) are taken in order until the time budget is spent (at least
@@ -75,8 +75,8 @@ def cpu_baseline(w, q, k, v, seconds: float):
             qn = W.to_f64(q[b:b + 1, h:h + 1])
             kn = W.to_f64(k[b:b + 1, h:h + 1])
             vn = W.to_f64(v[b:b + 1, h:h + 1])
-            attention_forward(qn, kn, vn, w.scale)
-            flops += 4.0 * w.S * w.S * w.D
+            attention_forward(qn, kn, vn, w.scale, causal_offset=0 if causal else None)
+            flops += 4.0 * w.D * (w.S * (w.S + 1) / 2 if causal else w.S * w.S)
             heads += 1
             if time.perf_counter() - t0 >= seconds:
                 break
@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--kv-splits", type=int, default=-1,
                     help="-1: attn_fwd; 0: attn_fwd_split with the library's split count; "
                          "n > 0: attn_fwd_split with at most n key ranges (partials + merge)")
+    ap.add_argument("--causal", action="store_true",
+                    help="causal mask (query i sees keys j <= i); FLOPs count visible scores only")
     ap.add_argument("--layout", choices=["bhsd", "bshd"], default="bhsd",
                     help="bshd: inputs and output stored token-major [B, S, H, D], run through "
                          "attn_fwd_strided without conversion copies")
@@ -176,11 +178,14 @@ def main():
     def step():
         if args.kv_splits >= 0:
             da.attn_fwd_split(qd, kd, vd, od, lsed, w.scale, kv_splits=args.kv_splits,
-                              workspace=ws, stream=stream, variant=args.variant)
+                              workspace=ws, stream=stream, variant=args.variant,
+                              causal=args.causal)
         elif args.layout == "bshd":
-            da.attn_fwd_strided(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant)
+            da.attn_fwd_strided(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant,
+                                causal=args.causal)
         else:
-            da.attn_fwd_ex(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant)
+            da.attn_fwd_ex(qd, kd, vd, od, lsed, w.scale, stream=stream, variant=args.variant,
+                           causal=args.causal)
 
     # Clock settle (untimed): the first ~100 ms of load run at transitional clocks.
     t_settle = time.perf_counter()
@@ -203,11 +208,13 @@ def main():
     kernel_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps      # average launch duration
     step_s = wall / args.steps
 
-    flops = w.flops
+    # 4·D FLOP per visible score: B·H·S² without a mask, B·H·S(S+1)/2 with it.
+    flops = w.flops if not args.causal else 4.0 * w.D * w.B * w.H * w.S * (w.S + 1) / 2
     value = flops / step_s / 1e12
     achieved = flops / kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    cfg = da.attn_get_config(w.B, w.H, w.S, w.D, q.dtype, variant=args.variant)
+    cfg = da.attn_get_config(w.B, w.H, w.S, w.D, q.dtype, variant=args.variant,
+                             causal=args.causal)
 
     out = {
         "metric": METRIC,
@@ -225,7 +232,7 @@ def main():
         "config": dict(w.as_dict(), kernel=cfg, api=("attn_fwd" if args.kv_splits < 0 and args.layout == "bhsd"
                                                      else "attn_fwd_strided" if args.kv_splits < 0
                                                      else f"attn_fwd_split(kv_splits={args.kv_splits})"),
-                       layout=args.layout),
+                       layout=args.layout, causal=args.causal),
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {
             "bound": "mfma",
@@ -238,7 +245,7 @@ def main():
         "cpu_baseline": None,
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, args.causal)
     print(json.dumps(out), flush=True)
 
 

@@ -48,7 +48,8 @@ class AttnError(RuntimeError):
 
 class attn_fwd_options(ctypes.Structure):
     _fields_ = [("rescale_threshold", ctypes.c_float), ("variant", ctypes.c_int),
-                ("grid", ctypes.c_int), ("reserved", ctypes.c_int * 4)]
+                ("grid", ctypes.c_int), ("causal", ctypes.c_int), ("causal_offset", ctypes.c_int),
+                ("reserved", ctypes.c_int * 2)]
 
 
 class attn_layout(ctypes.Structure):
@@ -129,16 +130,23 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
 
 
-def _options(rescale_threshold, variant, grid):
+def _options(rescale_threshold, variant, grid, causal=False):
+    """causal: False (no mask), True (last query row sees every key) or an int
+    offset (query row i sees keys j <= i + offset)."""
     opts = attn_fwd_options()
     opts.rescale_threshold = -1.0 if rescale_threshold is None else float(rescale_threshold)
     opts.variant = int(variant)
     opts.grid = int(grid)
+    if causal is True:
+        opts.causal = 1
+    elif causal is not False and causal is not None:
+        opts.causal = 2
+        opts.causal_offset = int(causal)
     return opts
 
 
 def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_lse=True,
-                rescale_threshold=None, variant=0, grid=0):
+                rescale_threshold=None, variant=0, grid=0, causal=False):
     """O = softmax(scale·Q·Kᵀ)·V (and the fp32 LSE) for contiguous [B, H, S, D] tensors.
 
     ``o`` and ``lse`` are allocated with torch when not given.  ``stream`` is a
@@ -173,7 +181,7 @@ def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_ls
         scale = 1.0 / math.sqrt(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    opts = _options(rescale_threshold, variant, grid)
+    opts = _options(rescale_threshold, variant, grid, causal)
     with torch.cuda.device(q.device):
         st = lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                              lse.data_ptr() if lse is not None else None, B, H, S, D,
@@ -182,17 +190,20 @@ def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_ls
     return o, lse
 
 
-def attn_fwd(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_lse=True):
+def attn_fwd(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_lse=True,
+             causal=False):
     """The library's default attention forward; see attn_fwd_ex."""
-    return attn_fwd_ex(q, k, v, o, lse, scale, stream=stream, return_lse=return_lse)
+    return attn_fwd_ex(q, k, v, o, lse, scale, stream=stream, return_lse=return_lse,
+                       causal=causal)
 
 
-def attn_get_config(B, H, S, D, dtype, *, rescale_threshold=None, variant=0, grid=0) -> dict:
+def attn_get_config(B, H, S, D, dtype, *, rescale_threshold=None, variant=0, grid=0,
+                    causal=False) -> dict:
     """Launch configuration for the current device (needs a gfx950 GPU)."""
     lib = load_library()
     code = dtype if isinstance(dtype, int) else _dtype_code_from_torch(dtype)
     out = attn_config()
-    opts = _options(rescale_threshold, variant, grid)
+    opts = _options(rescale_threshold, variant, grid, causal)
     _check(lib, lib.attn_get_config(B, H, S, D, code, ctypes.byref(opts), ctypes.byref(out)))
     return {name: getattr(out, name) for name, _ in attn_config._fields_}
 
@@ -246,7 +257,7 @@ def _lse_buffer(lse, shape, device, required=False):
 
 
 def attn_fwd_strided(q, k, v, o=None, lse=None, scale=None, *, stream=None, return_lse=True,
-                     rescale_threshold=None, variant=0, grid=0):
+                     rescale_threshold=None, variant=0, grid=0, causal=False):
     """Attention over strided [B, H, S, D] views (e.g. BSHD storage seen through
     ``x.transpose(1, 2)``); k and v may have their own length Skv.
 
@@ -267,7 +278,7 @@ def attn_fwd_strided(q, k, v, o=None, lse=None, scale=None, *, stream=None, retu
         scale = 1.0 / math.sqrt(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    opts = _options(rescale_threshold, variant, grid)
+    opts = _options(rescale_threshold, variant, grid, causal)
     ql, kl, vl, ol = _layout(q), _layout(k), _layout(v), _layout(o)
     with torch.cuda.device(q.device):
         st = lib.attn_fwd_strided(q.data_ptr(), ctypes.byref(ql), k.data_ptr(), ctypes.byref(kl),
@@ -280,7 +291,7 @@ def attn_fwd_strided(q, k, v, o=None, lse=None, scale=None, *, stream=None, retu
 
 
 def attn_fwd_partial(q, k, v, o_part=None, lse_part=None, scale=None, *, stream=None,
-                     rescale_threshold=None, variant=0, grid=0):
+                     rescale_threshold=None, variant=0, grid=0, causal=False):
     """Attention of q over the keys k, v of one range, as fp32 (o_part, lse_part):
     o_part normalised within the range, lse_part = ln Σ_range exp(scale·q·k).
     Inputs may be strided views (a key slice ``k[:, :, a:b]`` is one)."""
@@ -298,7 +309,7 @@ def attn_fwd_partial(q, k, v, o_part=None, lse_part=None, scale=None, *, stream=
         scale = 1.0 / math.sqrt(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    opts = _options(rescale_threshold, variant, grid)
+    opts = _options(rescale_threshold, variant, grid, causal)
     ql, kl, vl = _layout(q), _layout(k), _layout(v)
     with torch.cuda.device(q.device):
         st = lib.attn_fwd_partial(q.data_ptr(), ctypes.byref(ql), k.data_ptr(), ctypes.byref(kl),
@@ -346,7 +357,8 @@ def attn_fwd_split_workspace_size(B, H, S, D, kv_splits=0) -> int:
 
 
 def attn_fwd_split(q, k, v, o=None, lse=None, scale=None, *, kv_splits=0, workspace=None,
-                   stream=None, return_lse=True, rescale_threshold=None, variant=0, grid=0):
+                   stream=None, return_lse=True, rescale_threshold=None, variant=0, grid=0,
+                   causal=False):
     """attn_fwd with the keys of each item split into kv_splits ranges (0 = the
     library's choice) and merged; contiguous [B, H, S, D] tensors.  The fp32
     workspace is allocated with torch when not given."""
@@ -369,7 +381,7 @@ def attn_fwd_split(q, k, v, o=None, lse=None, scale=None, *, kv_splits=0, worksp
         scale = 1.0 / math.sqrt(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    opts = _options(rescale_threshold, variant, grid)
+    opts = _options(rescale_threshold, variant, grid, causal)
     with torch.cuda.device(q.device):
         st = lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                 lse.data_ptr() if lse is not None else None, B, H, S, D,

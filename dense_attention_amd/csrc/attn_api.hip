@@ -31,23 +31,30 @@ int fail(int status, const char* detail) {
   return status;
 }
 
-typedef hipError_t (*launch_fn)(const Params&, bool neg, int grid, hipStream_t stream);
+typedef hipError_t (*launch_fn)(const Params&, bool neg, bool causal, int grid, hipStream_t stream);
 typedef hipError_t (*occ_fn)(int* blocks_per_cu);
 
 // Negative score multipliers use a separate instantiation (the running
-// maximum of c·s is then taken over min(s)).
+// maximum of c·s is then taken over min(s)), and so do causal masks.
 template <class T, class TL>
-hipError_t launch_impl(const Params& p, bool neg, int grid, hipStream_t stream) {
-  if (neg)
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, true>), dim3(grid), dim3(TL::NT), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, false>), dim3(grid), dim3(TL::NT), 0, stream, p);
+hipError_t launch_impl(const Params& p, bool neg, bool causal, int grid, hipStream_t stream) {
+  if (causal) {
+    if (neg)
+      hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, true, true>), dim3(grid), dim3(TL::NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, false, true>), dim3(grid), dim3(TL::NT), 0, stream, p);
+  } else {
+    if (neg)
+      hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, true, false>), dim3(grid), dim3(TL::NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, false, false>), dim3(grid), dim3(TL::NT), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
 template <class T, class TL>
 hipError_t occupancy_impl(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attn::attn_fwd_kernel<T, TL, false>,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attn::attn_fwd_kernel<T, TL, false, false>,
                                                        TL::NT, 0);
 }
 
@@ -139,6 +146,8 @@ struct Plan {
   int per_cu = 0;
   int num_cus = 0;
   float thr = kDefaultThreshold;
+  int causal = 0;        // 0 none, else the mask is on with diagonal offset coff
+  int coff = 0;
   bool empty = false;
 };
 
@@ -161,6 +170,7 @@ int plan_launch(int B, int H, int Sq, int Skv, int D, int dtype, float scale,
     if (opts->grid < 0) return fail(ATTN_ERR_ARG, "grid must be >= 0");
     if (!(opts->rescale_threshold <= 64.0f) && !(opts->rescale_threshold < 0.0f))
       return fail(ATTN_ERR_ARG, "rescale_threshold must be <= 64");
+    if (opts->causal < 0 || opts->causal > 2) return fail(ATTN_ERR_ARG, "causal must be 0, 1 or 2");
   }
   // Rows are indexed with 32-bit integers inside a head and work items with
   // 32-bit integers overall.
@@ -176,6 +186,8 @@ int plan_launch(int B, int H, int Sq, int Skv, int D, int dtype, float scale,
   plan->var = var;
   plan->var_index = (int)(var - kVariants);
   plan->thr = (opts && opts->rescale_threshold >= 0.0f) ? opts->rescale_threshold : kDefaultThreshold;
+  plan->causal = opts ? opts->causal : 0;
+  plan->coff = plan->causal == 2 ? opts->causal_offset : Skv - Sq;
   plan->n_qtiles = (Sq + var->block_m - 1) / var->block_m;
   plan->empty = ((int64_t)B * H * plan->n_qtiles == 0);
   if (!plan->empty && Skv == 0) return fail(ATTN_ERR_SHAPE, "queries need at least one key (Skv >= 1)");
@@ -208,7 +220,9 @@ int plan_launch(int B, int H, int Sq, int Skv, int D, int dtype, float scale,
   plan->n_items = base_items * plan->n_splits;
   if (!need_device) return ATTN_OK;
 
-  int grid = di->num_cus * plan->per_cu;
+  // Causal items differ widely in length: one workgroup per item, longest
+  // first, and the hardware hands them to compute units as these free up.
+  int grid = plan->causal ? plan->n_items : di->num_cus * plan->per_cu;
   if (opts && opts->grid > 0) grid = opts->grid;
   if (grid > plan->n_items) grid = plan->n_items;
   plan->grid = grid;
@@ -287,11 +301,12 @@ int launch_forward(const Forward& f, const Plan& plan, hipStream_t stream) {
   p.n_splits = plan.n_splits;
   p.split_len = plan.split_len;
   p.n_items = plan.n_items;
-  p.xcd_remap = (plan.grid % 8 == 0 && plan.grid >= 8) ? 1 : 0;
+  p.xcd_remap = (!plan.causal && plan.grid % 8 == 0 && plan.grid >= 8) ? 1 : 0;
   p.o_f32 = f.o_f32 ? 1 : 0;
+  p.coff = plan.coff;
   p.c = f.scale * kLog2e;
   p.thr = plan.thr;
-  hipError_t e = plan.var->launch(p, p.c < 0.0f, plan.grid, stream);
+  hipError_t e = plan.var->launch(p, p.c < 0.0f, plan.causal != 0, plan.grid, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, hipGetErrorString(e));
   return ATTN_OK;
 }

@@ -103,6 +103,7 @@ struct Params {
   int n_items;           // B * H * n_qtiles * n_splits
   int xcd_remap;         // 1: the grid is a multiple of 8, group items per XCD
   int o_f32;             // 1: O is stored in fp32, normalised within its KV range
+  int coff;              // causal: query row i sees keys j <= i + coff (absolute key index)
   float c;               // scale * log2(e): scores in log2 units are s * c
   float thr;             // lazy-rescale threshold (log2 units)
 };
@@ -280,11 +281,11 @@ using SAcc = f32x16_t[TL::QB][TL::BN / 32];
 template <class TL>
 using PFrag = uint32_t[TL::QB][TL::BN / 32][8];
 
-template <class T, class TL, bool QK, bool SM, bool MASK, bool NEG, bool PV>
+template <class T, class TL, bool QK, bool SM, bool MASK, bool NEG, bool PV, bool GUARD = false>
 __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
                                           const SAcc<TL>& s_in, SAcc<TL>& s_out,
                                           const PFrag<TL>& p_in, PFrag<TL>& p_out,
-                                          float (&alpha)[TL::QB], int kb, int S, float c,
+                                          float (&alpha)[TL::QB], int kb, int klim, float c,
                                           float thr, int lane) {
   constexpr int QB = TL::QB, NB = TL::BN / 32, DT = TL::D / 16, DB = TL::D / 32;
   constexpr int NQ = NB * DT;        // K fragments (QK MFMA groups) per tile
@@ -340,9 +341,11 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
     for (int j = 0; j < VD && j < NP; ++j) vf[j] = vfrag(j);
   }
 
-  // softmax state.  Key kb + 16·hh + 32·nb + i of a tile is valid iff
-  // 32·nb + i < lim; lim is opaque so the compares stay inside the step.
-  int lim = S - (kb + 16 * (lane >> 5));
+  // softmax state.  Keys below klim (this lane's limit, counted from the
+  // start of the key range) are valid: key kb + 16·hh + 32·nb + i of a tile
+  // is valid iff 32·nb + i < lim; lim is opaque so the compares stay inside
+  // the step.
+  int lim = klim - (kb + 16 * (lane >> 5));
   if (MASK) asm volatile("" : "+v"(lim));
   constexpr float kInit = NEG ? __builtin_inff() : -__builtin_inff();
   float mx[QB], nm[QB], ls[QB][2];
@@ -394,10 +397,13 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
           const float mold = ws.m[qb];
           const bool rebase = (mold == -__builtin_inff()) || (mcand > mold + thr);
           const float mnew = rebase ? mcand : mold;
-          alpha[qb] = __builtin_amdgcn_exp2f(mold - mnew);  // 1 if kept, 0 on the first tile
+          // A row that has seen no valid key yet keeps m = -inf; it then
+          // measures p against 0 so that no (-inf) - (-inf) is formed.
+          const float mref = (GUARD && mnew == -__builtin_inff()) ? 0.f : mnew;
+          alpha[qb] = __builtin_amdgcn_exp2f(mold - mref);  // 1 if kept, 0 on the first tile
           any = any || (__builtin_amdgcn_ballot_w64(rebase) != 0);
           ws.m[qb] = mnew;
-          nm[qb] = -mnew;
+          nm[qb] = -mref;
           ls[qb][0] = 0.f;
           ls[qb][1] = 0.f;
         }
@@ -503,7 +509,8 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
     const float lt = lane_pair_sum(ws.l[qb]);
     const int row = qt * TL::BM + (wave * QB + qb) * 32 + lr;
     if (row < p.Sq) {
-      const float inv = 1.0f / lt;
+      // lt == 0 only for a row without any valid key (causal): O = 0, LSE = -inf.
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       const long long ro = o_off + (long long)row * p.o_ss;
       if (p.o_f32) {
         float* orow = static_cast<float*>(p.o) + ro;
@@ -532,7 +539,8 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
       }
       if (p.lse != nullptr && hh == 0) {
         // ln(sum_j exp(s_j * scale)) = (m + log2(l)) * ln 2
-        p.lse[lse_off + row] = (ws.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
+        p.lse[lse_off + row] = lt > 0.f ? (ws.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f
+                                        : -__builtin_inff();
       }
     }
   }
@@ -565,28 +573,40 @@ __device__ __forceinline__ void mfma_phase(WaveState<TL>& ws, const lds_t* kl, c
                                               0.f, lane);
 }
 
-template <class T, class TL, bool MASK, bool NEG>
-__device__ __forceinline__ void valu_phase(WaveState<TL>& ws, int i, int S, float c, float thr,
+template <class T, class TL, bool MASK, bool NEG, bool GUARD>
+__device__ __forceinline__ void valu_phase(WaveState<TL>& ws, int i, int klim, float c, float thr,
                                            SAcc<TL>& sacc, PFrag<TL>& pfr, int lane) {
   float alpha[TL::QB];
-  const bool any = pipe_step<T, TL, false, true, MASK, NEG, false>(
-      ws, nullptr, nullptr, sacc, sacc, pfr, pfr, alpha, i * TL::BN, S, c, thr, lane);
+  const bool any = pipe_step<T, TL, false, true, MASK, NEG, false, GUARD>(
+      ws, nullptr, nullptr, sacc, sacc, pfr, pfr, alpha, i * TL::BN, klim, c, thr, lane);
   // O has received P·V of tile i-1 and not yet that of tile i.
   if (any) rescale_o(ws, alpha);
 }
 
-template <class T, class TL, bool NEG>
+template <class T, class TL, bool NEG, bool CAUSAL>
 __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& cp, lds_t* smem,
                                              int item, int wave, int lane) {
   constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, DB = D / 32, DT = D / 16;
+  static_assert(!CAUSAL || QB == 1, "causal masks assume one 32-query block per wave");
   const int lr = lane & 31;
   const int hh = lane >> 5;
-  // Item -> (KV range sp, head bh, query tile qt); consecutive items are the
-  // query tiles of one head and one KV range.
-  const int qt = item % p.n_qtiles;
-  const int t_ = item / p.n_qtiles;
-  const int bh = t_ % p.BH;
-  const int sp = t_ / p.BH;
+  // Item -> (KV range sp, head bh, query tile qt).  Non-causal: consecutive
+  // items are the query tiles of one head and one KV range.  Causal: the
+  // last (longest) query tiles of every head come first, so that workgroups
+  // dispatched in order start with the largest items; consecutive items are
+  // different heads, and head bh lands on XCD bh % 8 when B·H % 8 == 0.
+  int qt, t_, bh, sp;
+  if (CAUSAL) {
+    bh = item % p.BH;
+    t_ = item / p.BH;
+    qt = p.n_qtiles - 1 - t_ % p.n_qtiles;
+    sp = t_ / p.n_qtiles;
+  } else {
+    qt = item % p.n_qtiles;
+    t_ = item / p.n_qtiles;
+    bh = t_ % p.BH;
+    sp = t_ / p.BH;
+  }
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int k0 = sp * p.split_len;
@@ -604,9 +624,41 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   const uint16_t* __restrict__ qh = p.q + b * p.q_sb + h * p.q_sh;
   const uint16_t* __restrict__ kh = p.k + b * p.k_sb + h * p.k_sh + (long long)k0 * kss;
   const uint16_t* __restrict__ vh = p.v + b * p.v_sb + h * p.v_sh + (long long)k0 * vss;
-  const int nt = (S + BN - 1) / BN;
+  // Keys of the range visible to this item: all S, or with a causal mask the
+  // prefix that its last query row sees.  Whole tiles below t_mask are
+  // visible to every row of the item and carry no mask.
+  int nt, t_mask;
+  int klim = S;  // this lane's key limit, counted from the range start
+  if (CAUSAL) {
+    const int q_first = qt * TL::BM;
+    const int q_last = min(p.Sq, q_first + TL::BM) - 1;
+    const int seen = min(S, q_last + p.coff - k0 + 1);
+    nt = seen > 0 ? (seen + BN - 1) / BN : 0;
+    t_mask = min(max(q_first + p.coff - k0 + 1, 0), S) / BN;
+    const int row = q_first + wave * 32 + lr;
+    klim = min(S, max(row + p.coff - k0 + 1, 0));
+  } else {
+    nt = (S + BN - 1) / BN;
+    t_mask = S / BN;
+  }
   const bool ragged = (S % BN) != 0;
   const Ring<TL> ring{smem};
+  if (CAUSAL && nt == 0) {
+    // No query row of this item sees a key of the range: O = 0, LSE = -inf.
+    WaveState<TL> ws;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      ws.m[qb] = -__builtin_inff();
+      ws.l[qb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ws.o[qb][db][i] = 0.f;
+    }
+    store_output<T, TL>(p, ws, sp * p.o_split + b * p.o_sb + h * p.o_sh,
+                       sp * p.lse_split + (long long)bh * p.Sq, qt, wave, lane);
+    return;
+  }
 
   // Copy set c(t) = {K_t, V_{t-1}}: the tiles M(t) reads.  Each wave issues its
   // share; tiles that run past the last key are clamped.
@@ -688,16 +740,20 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     if (DEEP && grp == 0) wait_vmem();
     cset();
     if (masked)
-      valu_phase<T, TL, true, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
+      valu_phase<T, TL, true, NEG, CAUSAL>(ws, i, klim, c, thr, sacc, pfr, lane);
     else
-      valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
+      valu_phase<T, TL, false, NEG, CAUSAL>(ws, i, klim, c, thr, sacc, pfr, lane);
     if (!DEEP && grp == 0) wait_vmem();
     __syncthreads();
   };
-  step(0, [&]() { copy_set(ahead); }, nt == 1 && ragged);
-  // Steps 1 .. nt-4 copy only whole tiles and softmax unmasked tiles; the last
-  // three steps are peeled so the steady loop carries no such branches.
-  for (int i = 1; i <= nt - 4; ++i) {
+  // Tile i needs masks iff it is not a whole tile visible to every row.
+  auto masked = [&](int i) { return i >= t_mask || (i == nt - 1 && ragged); };
+  step(0, [&]() { copy_set(ahead); }, masked(0));
+  // Steps 1 .. steady copy only whole tiles and softmax unmasked tiles; the
+  // remaining (at least the last three) steps are peeled so the steady loop
+  // carries no such branches.
+  const int steady = CAUSAL ? min(nt - 4, t_mask - 1) : nt - 4;
+  for (int i = 1; i <= steady; ++i) {
     mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
     if (grp == 1) wait_vmem();
     __syncthreads();
@@ -705,12 +761,12 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     const int j = i + ahead;
     cp.k.issue(kh + (long long)(j * BN) * kss, ring.k(j), wave);
     cp.v.issue(vh + (long long)((j - 1) * BN) * vss, ring.v(j - 1), wave);
-    valu_phase<T, TL, false, NEG>(ws, i, S, c, thr, sacc, pfr, lane);
+    valu_phase<T, TL, false, NEG, CAUSAL>(ws, i, klim, c, thr, sacc, pfr, lane);
     if (!DEEP && grp == 0) wait_vmem();
     __syncthreads();
   }
-  for (int i = nt - 3 > 1 ? nt - 3 : 1; i < nt; ++i)
-    step(i, [&]() { copy_set(i + ahead); }, i == nt - 1 && ragged);
+  for (int i = steady + 1 > 1 ? steady + 1 : 1; i < nt; ++i)
+    step(i, [&]() { copy_set(i + ahead); }, masked(i));
   // Step nt: P·V of the last tile.
   mfma_phase<T, TL, false, true, NEG>(ws, nullptr, ring.v(nt - 1), sacc, pfr, lane);
   if (grp == 0) __syncthreads();  // group 1 has one barrier fewer to go
@@ -721,7 +777,7 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
 }
 
 
-template <class T, class TL, bool NEG>
+template <class T, class TL, bool NEG, bool CAUSAL>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 void attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[TL::LDS_BYTES];
@@ -743,7 +799,7 @@ void attn_fwd_kernel(Params p) {
     if (base >= p.n_items) break;
     int item = base + (int)blockIdx.x;
     if (p.xcd_remap) item = base + (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
-    if (item < p.n_items) process_item<T, TL, NEG>(p, cp, smem, item, wave, lane);
+    if (item < p.n_items) process_item<T, TL, NEG, CAUSAL>(p, cp, smem, item, wave, lane);
   }
 }
 

@@ -94,9 +94,20 @@ typedef struct attn_fwd_options {
    * attn_variant_info().  A variant must support D and dtype. */
   int variant;
   /* Persistent grid size in workgroups, 0 = the library's choice (all CUs at
-   * full occupancy, capped at the number of work items). */
+   * full occupancy, capped at the number of work items; with a causal mask,
+   * one workgroup per work item, the longest first). */
   int grid;
-  int reserved[4];  /* must be zero */
+  /* Causal mask.  0: none.  1: query row i (0-based) attends to keys
+   * j <= i + (Skv - Sq), i.e. the last query row sees every key (equal
+   * lengths: j <= i).  2: query row i attends to keys j <= i + causal_offset
+   * (for a shard of keys or queries cut out of a longer sequence).  A query
+   * row that sees no key gets O = 0 and LSE = -inf.  ("Attention for sm90,
+   * Line by Line", "What does the persistent flag do in the sm90 attention
+   * config?": the mask makes the work per query tile vary widely, which a
+   * static persistent schedule balances badly.) */
+  int causal;
+  int causal_offset;  /* used when causal == 2 */
+  int reserved[2];    /* must be zero */
 } attn_fwd_options_t;
 
 /* attn_fwd with options; opts == NULL behaves exactly like attn_fwd. */

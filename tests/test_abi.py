@@ -94,7 +94,7 @@ def test_rejects_null_and_misaligned(lib):
 def test_rejects_bad_options(lib):
     o = da.attn_fwd_options()
     o.rescale_threshold = -1.0
-    o.reserved[2] = 1
+    o.reserved[1] = 1
     assert _call(lib, opts=o) == -8
     o = da.attn_fwd_options()
     o.rescale_threshold = 100.0
@@ -227,3 +227,17 @@ def test_split_validation_and_workspace_size(lib):
     assert lib.attn_fwd_split_workspace_size(1, 1, 4096, 64, 0) == up(16 * 4096 * 64 * 4) + up(16 * 4096 * 4)
     assert lib.attn_fwd_split_workspace_size(1, 1, 100, 64, 0) == up(100 * 64 * 4) + up(100 * 4)
     assert lib.attn_fwd_split_workspace_size(1, 1, 100, 96, 1) == 0
+
+
+def test_causal_option_validation(lib):
+    opts = da.attn_fwd_options()
+    opts.rescale_threshold = -1
+    opts.causal = 3
+    assert _call(lib, opts=opts) == -8
+    opts.causal = -1
+    assert _call(lib, opts=opts) == -8
+    # Python side: True -> 1, an int -> 2 with that offset, False -> 0
+    assert da._options(None, 0, 0, True).causal == 1
+    o = da._options(None, 0, 0, -7)
+    assert (o.causal, o.causal_offset) == (2, -7)
+    assert da._options(None, 0, 0, False).causal == 0
