@@ -67,6 +67,7 @@ struct Variant {
   int waves;
   int stages;
   int lds_bytes;
+  int key_split;
   launch_fn launch;
   occ_fn occupancy;
 };
@@ -74,11 +75,12 @@ struct Variant {
 template <class T, int DTYPE, class TL>
 constexpr Variant make_variant(int id) {
   return Variant{id, DTYPE, TL::D, TL::BM, TL::BN, TL::NW, TL::STAGES, TL::LDS_BYTES,
-                 &launch_impl<T, TL>, &occupancy_impl<T, TL>};
+                 TL::KSPLIT ? 1 : 0, &launch_impl<T, TL>, &occupancy_impl<T, TL>};
 }
 
-// Tile variants: ids are stable; the first matching entry for (D, dtype) in
-// kDefaults is the library's choice.
+// Tile variants; ids are stable.  8 waves (256 query rows, two groups sharing
+// one K/V stream), 4 waves (128 rows, one wave per SIMD), and 8 waves with a
+// key split (128 rows, each group streaming half of the keys).
 const Variant kVariants[] = {
     make_variant<BF16, ATTN_BF16, Tile<128, 64, 8, 1>>(1),
     make_variant<F16, ATTN_F16, Tile<128, 64, 8, 1>>(2),
@@ -88,6 +90,10 @@ const Variant kVariants[] = {
     make_variant<F16, ATTN_F16, Tile<128, 64, 4, 1>>(6),
     make_variant<BF16, ATTN_BF16, Tile<64, 64, 8, 1>>(7),
     make_variant<F16, ATTN_F16, Tile<64, 64, 8, 1>>(8),
+    make_variant<BF16, ATTN_BF16, Tile<64, 64, 8, 1, true>>(9),
+    make_variant<F16, ATTN_F16, Tile<64, 64, 8, 1, true>>(10),
+    make_variant<BF16, ATTN_BF16, Tile<128, 64, 8, 1, true>>(11),
+    make_variant<F16, ATTN_F16, Tile<128, 64, 8, 1, true>>(12),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -97,10 +103,21 @@ const Variant* find_variant(int id) {
   return nullptr;
 }
 
-const Variant* default_variant(int D, int dtype) {
-  for (int i = 0; i < kNumVariants; ++i)
-    if (kVariants[i].D == D && kVariants[i].dtype == dtype) return &kVariants[i];
-  return nullptr;
+// The library's choice: the 8-wave tiling with 256-row items, unless its
+// items are too few to fill the device; then the key-split tiling, whose
+// 128-row items take about half as long each.  Compared in rounds of one
+// workgroup per compute unit, with 10% for the key split's merge.
+const Variant* default_variant(int D, int dtype, int64_t BH, int Sq, int num_cus) {
+  const int shared_id = D == 128 ? (dtype == ATTN_BF16 ? 1 : 2) : (dtype == ATTN_BF16 ? 7 : 8);
+  const int split_id = D == 128 ? (dtype == ATTN_BF16 ? 11 : 12) : (dtype == ATTN_BF16 ? 9 : 10);
+  const Variant* a = find_variant(shared_id);
+  const Variant* k = find_variant(split_id);
+  if (num_cus <= 0) num_cus = 256;
+  const int64_t items_a = BH * ((Sq + a->block_m - 1) / a->block_m);
+  const int64_t items_k = BH * ((Sq + k->block_m - 1) / k->block_m);
+  const int64_t rounds_a = (items_a + num_cus - 1) / num_cus;
+  const int64_t rounds_k = (items_k + num_cus - 1) / num_cus;
+  return (rounds_k * 11 < rounds_a * 20) ? k : a;
 }
 
 // Per-device facts, read once per device.
@@ -177,14 +194,23 @@ int plan_launch(int B, int H, int Sq, int Skv, int D, int dtype, float scale,
   if ((int64_t)B * H * (int64_t)Sq >= (int64_t)1 << 31 || Skv >= (1 << 30))
     return fail(ATTN_ERR_SHAPE, "B*H*Sq must be < 2^31 and Skv < 2^30");
 
-  const Variant* var = default_variant(D, dtype);
+  const DeviceInfo* di = nullptr;
+  if (need_device || kv_splits == 0) {
+    int st = device_info(&di);
+    if (st != ATTN_OK) return st;
+    plan->num_cus = di->num_cus;
+  }
+  const Variant* var = nullptr;
   if (opts && opts->variant != 0) {
     var = find_variant(opts->variant);
     if (!var) return fail(ATTN_ERR_ARG, "unknown variant id");
     if (var->D != D || var->dtype != dtype) return fail(ATTN_ERR_ARG, "variant does not support this D/dtype");
+  } else {
+    var = default_variant(D, dtype, (int64_t)B * H, Sq, plan->num_cus);
   }
   plan->var = var;
   plan->var_index = (int)(var - kVariants);
+  if (di) plan->per_cu = di->occupancy[plan->var_index];
   plan->thr = (opts && opts->rescale_threshold >= 0.0f) ? opts->rescale_threshold : kDefaultThreshold;
   plan->causal = opts ? opts->causal : 0;
   plan->coff = plan->causal == 2 ? opts->causal_offset : Skv - Sq;
@@ -192,14 +218,6 @@ int plan_launch(int B, int H, int Sq, int Skv, int D, int dtype, float scale,
   plan->empty = ((int64_t)B * H * plan->n_qtiles == 0);
   if (!plan->empty && Skv == 0) return fail(ATTN_ERR_SHAPE, "queries need at least one key (Skv >= 1)");
   const int base_items = B * H * plan->n_qtiles;
-
-  const DeviceInfo* di = nullptr;
-  if (need_device || kv_splits == 0) {
-    int st = device_info(&di);
-    if (st != ATTN_OK) return st;
-    plan->num_cus = di->num_cus;
-    plan->per_cu = di->occupancy[plan->var_index];
-  }
   // KV ranges: whole tiles, at least kMinSplitKeys keys each when chosen here.
   int want = kv_splits;
   if (want == 0) {
@@ -520,7 +538,7 @@ int attn_get_config(int B, int H, int S, int D, int dtype, const attn_fwd_option
 int attn_variant_count(void) { return kNumVariants; }
 
 int attn_variant_info(int index, int* id, int* head_dim, int* dtype, int* block_m, int* block_n,
-                      int* waves, int* stages) {
+                      int* waves, int* stages, int* key_split) {
   if (index < 0 || index >= kNumVariants) return fail(ATTN_ERR_ARG, "variant index out of range");
   const Variant& v = kVariants[index];
   if (id) *id = v.id;
@@ -530,6 +548,7 @@ int attn_variant_info(int index, int* id, int* head_dim, int* dtype, int* block_
   if (block_n) *block_n = v.block_n;
   if (waves) *waves = v.waves;
   if (stages) *stages = v.stages;
+  if (key_split) *key_split = v.key_split;
   return ATTN_OK;
 }
 

@@ -114,26 +114,42 @@ struct Params {
 __device__ __forceinline__ int lane_key(int r) {
   return (((r >> 2) & 1) << 4) | ((r >> 3) << 2) | (r & 3);
 }
-template <int D_, int BN_, int NW_, int QB_>
+// KSPLIT: the two groups of four waves of an 8-wave workgroup hold the same
+// query rows and each streams one half of the item's keys through a K/V ring
+// of its own; their partial results are merged through LDS at the end of the
+// item.  This keeps two waves on every SIMD (the ping-pong below) with
+// 128-row work items, for problems with too few 256-row items to fill the
+// device.
+template <int D_, int BN_, int NW_, int QB_, bool KSPLIT_ = false>
 struct Tile {
   static constexpr int D = D_;
   static constexpr int BN = BN_;            // keys per K/V tile
   static constexpr int NW = NW_;            // waves per workgroup
   static constexpr int QB = QB_;            // 32-query blocks per wave
+  static constexpr bool KSPLIT = KSPLIT_;
+  static constexpr int GW = KSPLIT ? NW / 2 : NW;  // waves sharing one K/V stream
   static constexpr int NT = NW * 64;        // threads per workgroup
-  static constexpr int BM = NW * QB * 32;   // query rows per work item
+  static constexpr int BM = GW * QB * 32;   // query rows per work item
   static constexpr int DC = D / 8;          // 16-byte chunks per row
   static constexpr int KS = D * 2 + 16;     // LDS row stride of K (bytes)
   static constexpr int VS = D * 2 + 64;     // LDS row stride of V (bytes)
   static constexpr int K_TILE = BN * KS;
   static constexpr int V_TILE = BN * VS;
+  static constexpr int RINGS = KSPLIT ? 2 : 1;
   // K/V ring depth: three tiles when they fit in LDS, else two.
-  static constexpr int STAGES = 3 * (BN * (KS + VS)) <= 160 * 1024 ? 3 : 2;
-  static constexpr int LDS_BYTES = STAGES * (K_TILE + V_TILE);
+  static constexpr int STAGES = 3 * RINGS * (BN * (KS + VS)) <= 160 * 1024 ? 3 : 2;
+  static constexpr int RING_BYTES = STAGES * (K_TILE + V_TILE);
+  static constexpr int LDS_BYTES = RINGS * RING_BYTES;
+  // Per-lane 16-byte chunks one wave hands over in the key-split merge: the
+  // O accumulators, then (m, l) of each query block.
+  static constexpr int XCH = QB * (D / 32) * 4 + 1;
   // Waves per SIMD the register allocation targets.
   static constexpr int WPE = NW / 4;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile sizes");
   static_assert(K_TILE % 1024 == 0 && V_TILE % 1024 == 0, "tiles must be whole DMA blocks");
+  static_assert(!KSPLIT || NW == 8, "a key split pairs two groups of four waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(!KSPLIT || GW * XCH * 1024 <= LDS_BYTES, "merge exchange must fit in the rings");
 };
 
 // One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane i
@@ -155,8 +171,8 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const lds
 }
 
 // HBM -> LDS copy of one K or V tile (rows kb .. kb+BN-1 of one head) into a
-// padded LDS tile of row stride STRIDE.  Each wave owns BPW of the tile's
-// 1 KiB blocks; lane i of a block fills 16-byte slot i.  With LANE_ORDER, LDS
+// padded LDS tile of row stride STRIDE.  Each of the GW waves that share the
+// stream owns BPW of the tile's 1 KiB blocks (`wave` is the index among them); lane i of a block fills 16-byte slot i.  With LANE_ORDER, LDS
 // row p of each 32-row block receives key lane_key(p).  Pad slots are not
 // loaded.  The per-lane byte offsets do not depend on the tile, so they are
 // computed once per kernel and a full tile costs one address add per block.
@@ -164,7 +180,7 @@ template <class TL, int STRIDE, bool LANE_ORDER>
 struct DmaPlan {
   static constexpr int SPR = STRIDE / 16;              // 16-byte slots per LDS row
   static constexpr int BLOCKS = TL::BN * SPR / 64;     // 1 KiB blocks per tile
-  static constexpr int BPW = (BLOCKS + TL::NW - 1) / TL::NW;
+  static constexpr int BPW = (BLOCKS + TL::GW - 1) / TL::GW;
   // Byte offset of this lane's chunk from the tile's first row.  Pad slots load
   // chunk 0 of their row again (the pad bytes of an LDS row are never read).
   uint32_t off[BPW];
@@ -192,7 +208,7 @@ struct DmaPlan {
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
       const int blk = wave * BPW + t;
-      if (BLOCKS % TL::NW == 0 || blk < BLOCKS) {
+      if (BLOCKS % TL::GW == 0 || blk < BLOCKS) {
         // Opaque per call: keeps the address as uniform base + 32-bit lane
         // offset instead of a hoisted 64-bit per-lane pointer.
         dma16(tile, off[t], dst + blk * 1024);
@@ -209,7 +225,7 @@ struct DmaPlan {
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
       const int blk = wave * BPW + t;
-      if (BLOCKS % TL::NW == 0 || blk < BLOCKS) {
+      if (BLOCKS % TL::GW == 0 || blk < BLOCKS) {
         int key, c;
         slot_rc(blk, lane, key, c);
         key = min(key, rows - 1);
@@ -232,11 +248,21 @@ __device__ __forceinline__ u32x4_t ld_lds16(const lds_t* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(p);
 }
 
+__device__ __forceinline__ void st_lds16(lds_t* p, u32x4_t x) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(p) = x;
+}
+
 __device__ __forceinline__ u32x2_t ld_lds_tr(const lds_t* p) {
   i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4_t*)(p));
   return __builtin_bit_cast(u32x2_t, r);
 }
+
+// Bit casts through by-value parameters.  __builtin_bit_cast applied directly
+// to an element of an ext_vector_type value (v[i]) reads the vector's first
+// element instead; a by-value argument is a plain float or uint32_t.
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
 
 __device__ __forceinline__ float lane_pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
@@ -499,7 +525,7 @@ struct Copies {
 // partial result over one KV range) and the LSE.
 template <class T, class TL>
 __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL>& ws,
-                                             long long o_off, long long lse_off, int qt, int wave,
+                                             long long o_off, long long lse_off, int qt, int qw,
                                              int lane) {
   constexpr int QB = TL::QB, DB = TL::D / 32;
   const int lr = lane & 31;
@@ -507,7 +533,7 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lane_pair_sum(ws.l[qb]);
-    const int row = qt * TL::BM + (wave * QB + qb) * 32 + lr;
+    const int row = qt * TL::BM + (qw * QB + qb) * 32 + lr;
     if (row < p.Sq) {
       // lt == 0 only for a row without any valid key (causal): O = 0, LSE = -inf.
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -520,7 +546,7 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
           for (int j = 0; j < 4; ++j) {
             u32x4_t w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(uint32_t, ws.o[qb][db][4 * j + e] * inv);
+            for (int e = 0; e < 4; ++e) w[e] = f2u(ws.o[qb][db][4 * j + e] * inv);
             *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh + 4 * j) = w;
           }
       } else {
@@ -583,13 +609,87 @@ __device__ __forceinline__ void valu_phase(WaveState<TL>& ws, int i, int klim, f
   if (any) rescale_o(ws, alpha);
 }
 
+// Key-split merge: group 1 hands its (m, l, O) to the wave of group 0 that
+// holds the same query rows, through LDS (the rings are idle at this point),
+// and group 0 combines the two partial results of each row:
+//   m = max(m0, m1),  l = l0·2^(m0-m) + l1·2^(m1-m),  O = O0·2^(m0-m) + O1·2^(m1-m).
+// (The associative merge of partial softmax results: "Attention for sm90, Line
+// by Line", the split-KV discussion, and the running-max algebra of "B200
+// Attention Kernel from Scratch to Near-SOTA in 60 Diagrams", Chapter 1.)
+template <class TL>
+__device__ __forceinline__ void merge_key_halves(WaveState<TL>& ws, lds_t* smem, int grp, int qw,
+                                                 int lane) {
+  constexpr int QB = TL::QB, DB = TL::D / 32;
+  lds_t* xb = smem + (qw * TL::XCH * 64 + lane) * 16;
+  auto slot = [&](int c) { return xb + c * 1024; };
+  if (grp == 1) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t w = {f2u(ws.o[qb][db][4 * j]), f2u(ws.o[qb][db][4 * j + 1]),
+                             f2u(ws.o[qb][db][4 * j + 2]), f2u(ws.o[qb][db][4 * j + 3])};
+          st_lds16(slot((qb * DB + db) * 4 + j), w);
+        }
+    static_assert(QB <= 2, "(m, l) of every query block share one chunk");
+    u32x4_t ml = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      ml[2 * qb] = f2u(ws.m[qb]);
+      ml[2 * qb + 1] = f2u(ws.l[qb]);
+    }
+    st_lds16(slot(TL::XCH - 1), ml);
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const u32x4_t ml = ld_lds16(slot(TL::XCH - 1));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m1 = u2f(ml[2 * qb]);
+      const float l1 = u2f(ml[2 * qb + 1]);
+      const float m0 = ws.m[qb];
+      const float mm = fmaxf(m0, m1);
+      // A row without a visible key in either half keeps m = -inf and l = 0.
+      const bool none = mm == -__builtin_inff();
+      const float a0 = none ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
+      const float a1 = none ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+      ws.m[qb] = mm;
+      ws.l[qb] = ws.l[qb] * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t w = ld_lds16(slot((qb * DB + db) * 4 + j));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ws.o[qb][db][4 * j + e] =
+                __builtin_fmaf(ws.o[qb][db][4 * j + e], a0, u2f(w[e]) * a1);
+        }
+    }
+  }
+  // The exchange area is ring memory again for the next item's copies.
+  __syncthreads();
+}
+
 template <class T, class TL, bool NEG, bool CAUSAL>
 __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& cp, lds_t* smem,
                                              int item, int wave, int lane) {
   constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, DB = D / 32, DT = D / 16;
+  constexpr bool KSPLIT = TL::KSPLIT;
   static_assert(!CAUSAL || QB == 1, "causal masks assume one 32-query block per wave");
   const int lr = lane & 31;
   const int hh = lane >> 5;
+  // Wave groups: waves w and w+4 share a SIMD.  grp decides the slot offset
+  // of the ping-pong schedule.  Without a key split the groups hold different
+  // query rows and consume one K/V stream, whose copies they share; group 1
+  // trails by one slot.  With a key split both groups hold the same query rows
+  // (qw) and each streams its own keys, so each runs the leading group's copy
+  // schedule on its own ring (`lead`).
+  const int grp = TL::NW == 8 ? (wave >> 2) : 0;
+  const int qw = KSPLIT ? (wave & 3) : wave;
+  const bool lead = KSPLIT || grp == 0;
   // Item -> (KV range sp, head bh, query tile qt).  Non-causal: consecutive
   // items are the query tiles of one head and one KV range.  Causal: the
   // last (longest) query tiles of every head come first, so that workgroups
@@ -617,13 +717,10 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   int S = min(p.Skv - k0, p.split_len);
   asm volatile("" : "+s"(S));
   const float c = p.c, thr = p.thr;
-  const int grp = TL::NW == 8 ? (wave >> 2) : 0;
   const int kss = p.k_ss, vss = p.v_ss;
   const uint32_t krb = (uint32_t)kss * 2u, vrb = (uint32_t)vss * 2u;
 
   const uint16_t* __restrict__ qh = p.q + b * p.q_sb + h * p.q_sh;
-  const uint16_t* __restrict__ kh = p.k + b * p.k_sb + h * p.k_sh + (long long)k0 * kss;
-  const uint16_t* __restrict__ vh = p.v + b * p.v_sb + h * p.v_sh + (long long)k0 * vss;
   // Keys of the range visible to this item: all S, or with a causal mask the
   // prefix that its last query row sees.  Whole tiles below t_mask are
   // visible to every row of the item and carry no mask.
@@ -635,16 +732,16 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     const int seen = min(S, q_last + p.coff - k0 + 1);
     nt = seen > 0 ? (seen + BN - 1) / BN : 0;
     t_mask = min(max(q_first + p.coff - k0 + 1, 0), S) / BN;
-    const int row = q_first + wave * 32 + lr;
+    const int row = q_first + qw * 32 + lr;
     klim = min(S, max(row + p.coff - k0 + 1, 0));
   } else {
     nt = (S + BN - 1) / BN;
     t_mask = S / BN;
   }
   const bool ragged = (S % BN) != 0;
-  const Ring<TL> ring{smem};
   if (CAUSAL && nt == 0) {
     // No query row of this item sees a key of the range: O = 0, LSE = -inf.
+    if (KSPLIT && grp == 1) return;
     WaveState<TL> ws;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -656,40 +753,54 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
         for (int i = 0; i < 16; ++i) ws.o[qb][db][i] = 0.f;
     }
     store_output<T, TL>(p, ws, sp * p.o_split + b * p.o_sb + h * p.o_sh,
-                       sp * p.lse_split + (long long)bh * p.Sq, qt, wave, lane);
+                       sp * p.lse_split + (long long)bh * p.Sq, qt, qw, lane);
     return;
   }
+
+  // This group's tiles: all nt, or with a key split the first ceil(nt/2)
+  // (group 0) or the rest (group 1, starting at tile tb).  Sg and klg count
+  // keys from the group's first tile.
+  const int nt0 = KSPLIT ? (nt + 1) / 2 : nt;
+  const int tb = (KSPLIT && grp == 1) ? nt0 : 0;
+  const int ntg = (KSPLIT && grp == 1) ? nt - nt0 : nt0;
+  const int Sg = S - tb * BN;
+  const int klg = klim - tb * BN;
+  const uint16_t* __restrict__ kh = p.k + b * p.k_sb + h * p.k_sh + (long long)(k0 + tb * BN) * kss;
+  const uint16_t* __restrict__ vh = p.v + b * p.v_sb + h * p.v_sh + (long long)(k0 + tb * BN) * vss;
+  const Ring<TL> ring{smem + (KSPLIT ? grp * TL::RING_BYTES : 0)};
 
   // Copy set c(t) = {K_t, V_{t-1}}: the tiles M(t) reads.  Each wave issues its
   // share; tiles that run past the last key are clamped.
   auto copy_k = [&](int t) {
     const uint16_t* kt = kh + (long long)(t * BN) * kss;
-    if ((t + 1) * BN <= S)
-      cp.k.issue(kt, ring.k(t), wave);
+    if ((t + 1) * BN <= Sg)
+      cp.k.issue(kt, ring.k(t), qw);
     else
-      cp.k.issue_clamped(kt, S - t * BN, krb, ring.k(t), wave, lane);
+      cp.k.issue_clamped(kt, Sg - t * BN, krb, ring.k(t), qw, lane);
   };
   auto copy_v = [&](int t) {
     const uint16_t* vt = vh + (long long)(t * BN) * vss;
-    if ((t + 1) * BN <= S)
-      cp.v.issue(vt, ring.v(t), wave);
+    if ((t + 1) * BN <= Sg)
+      cp.v.issue(vt, ring.v(t), qw);
     else
-      cp.v.issue_clamped(vt, S - t * BN, vrb, ring.v(t), wave, lane);
+      cp.v.issue_clamped(vt, Sg - t * BN, vrb, ring.v(t), qw, lane);
   };
   auto copy_set = [&](int t) {
-    if (t < nt) copy_k(t);
-    if (t >= 1 && t <= nt) copy_v(t - 1);
+    if (t < ntg) copy_k(t);
+    if (t >= 1 && t <= ntg) copy_v(t - 1);
   };
 
   // Prologue: c(0) (and with a three-deep ring c(1)) in flight while Q is
   // loaded into registers.
   constexpr bool DEEP = TL::STAGES == 3;
-  copy_set(0);
-  if (DEEP) copy_set(1);
+  if (ntg > 0) {
+    copy_set(0);
+    if (DEEP) copy_set(1);
+  }
   WaveState<TL> ws;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = qt * TL::BM + (wave * QB + qb) * 32 + lr;
+    const int row = qt * TL::BM + (qw * QB + qb) * 32 + lr;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       u32x4_t x = {0u, 0u, 0u, 0u};
@@ -709,71 +820,83 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   // Slots: group 0 runs M(i) in slot 2i and V(i) in slot 2i+1, group 1 one
   // slot later.  Copies are issued only in V phases: in V(i) a wave issues its
   // share of c(i + ahead).  A wave's share of c(i+1) is complete before the
-  // barrier that ends slot 2i+1 (M(i+1) of group 0 reads it in slot 2i+2):
-  // group 1 waits at the end of M(i), group 0 in V(i).
-  //  * three-deep ring: ahead = 2 for both groups; group 0 waits at the start
-  //    of V(i).  c(i+2) overwrites K_{i-1} and V_{i-2}, last read in M(i-1)
-  //    (slots 2i-2 and 2i-1).
-  //  * two-deep ring: ahead = 1 for group 0, which waits at the end of V(i)
-  //    (after its softmax), and 2 for group 1.  c(i+1) issued in slot 2i+1
-  //    overwrites K_{i-1} and V_{i-2} (read in slots 2i-2, 2i-1); c(i+2)
-  //    issued by group 1 in slot 2i+2 overwrites K_i and V_{i-1} (read in
-  //    slots 2i, 2i+1).
-  // No DMA is issued or awaited inside group 0's MFMA phase.
-  const int ahead = (DEEP || grp == 1) ? 2 : 1;
+  // barrier that ends the slot before M(i+1): the leading schedule waits in
+  // V(i); group 1 of a shared stream waits at the end of M(i).
+  //  * three-deep ring: ahead = 2; the leading schedule waits at the start of
+  //    V(i).  c(i+2) overwrites K_{i-1} and V_{i-2}, last read in M(i-1),
+  //    two slots or more before V(i).
+  //  * two-deep ring: ahead = 1 for the leading schedule, which waits at the
+  //    end of V(i) (after its softmax), and 2 for group 1 of a shared stream.
+  //    c(i+1) issued in V(i) overwrites K_{i-1} and V_{i-2} (read in M(i-1),
+  //    which ends before V(i) of either group starts); c(i+2) issued by
+  //    group 1 of a shared stream in slot 2i+2 overwrites K_i and V_{i-1},
+  //    read in slots 2i and 2i+1.
+  // No DMA is issued or awaited inside a leading MFMA phase.
+  const int ahead = (DEEP || !lead) ? 2 : 1;
   SAcc<TL> sacc;
   PFrag<TL> pfr;
   if (grp == 1) {  // group 1 sits out slot 0
-    if (!DEEP) copy_set(1);
+    if (!lead && !DEEP) copy_set(1);
     __syncthreads();
   }
-  // One step i: M(i) (P·V of tile i-1 unless i == 0, Sᵀ of tile i), then V(i)
-  // (softmax of tile i, masked when it is a ragged last tile).  `cset`
-  // issues the step's copies.
-  auto step = [&](int i, auto cset, bool masked) {
-    if (i == 0)
-      mfma_phase<T, TL, true, false, NEG>(ws, ring.k(0), nullptr, sacc, pfr, lane);
-    else
+  if (ntg > 0) {
+    // One step i: M(i) (P·V of tile i-1 unless i == 0, Sᵀ of tile i), then
+    // V(i) (softmax of tile i, masked when it is not a whole tile visible to
+    // every row).  `cset` issues the step's copies.
+    auto step = [&](int i, auto cset, bool masked) {
+      if (i == 0)
+        mfma_phase<T, TL, true, false, NEG>(ws, ring.k(0), nullptr, sacc, pfr, lane);
+      else
+        mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
+      if (!lead) wait_vmem();
+      __syncthreads();
+      if (DEEP && lead) wait_vmem();
+      cset();
+      if (masked)
+        valu_phase<T, TL, true, NEG, CAUSAL>(ws, i, klg, c, thr, sacc, pfr, lane);
+      else
+        valu_phase<T, TL, false, NEG, CAUSAL>(ws, i, klg, c, thr, sacc, pfr, lane);
+      if (!DEEP && lead) wait_vmem();
+      __syncthreads();
+    };
+    auto masked = [&](int i) { return tb + i >= t_mask || (tb + i == nt - 1 && ragged); };
+    step(0, [&]() { copy_set(ahead); }, masked(0));
+    // Steps 1 .. steady copy only whole tiles and softmax unmasked tiles; the
+    // remaining (at least the last three) steps are peeled so the steady loop
+    // carries no such branches.
+    const int steady = CAUSAL ? min(ntg - 4, t_mask - tb - 1) : ntg - 4;
+    for (int i = 1; i <= steady; ++i) {
       mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
-    if (grp == 1) wait_vmem();
-    __syncthreads();
-    if (DEEP && grp == 0) wait_vmem();
-    cset();
-    if (masked)
-      valu_phase<T, TL, true, NEG, CAUSAL>(ws, i, klim, c, thr, sacc, pfr, lane);
-    else
-      valu_phase<T, TL, false, NEG, CAUSAL>(ws, i, klim, c, thr, sacc, pfr, lane);
-    if (!DEEP && grp == 0) wait_vmem();
-    __syncthreads();
-  };
-  // Tile i needs masks iff it is not a whole tile visible to every row.
-  auto masked = [&](int i) { return i >= t_mask || (i == nt - 1 && ragged); };
-  step(0, [&]() { copy_set(ahead); }, masked(0));
-  // Steps 1 .. steady copy only whole tiles and softmax unmasked tiles; the
-  // remaining (at least the last three) steps are peeled so the steady loop
-  // carries no such branches.
-  const int steady = CAUSAL ? min(nt - 4, t_mask - 1) : nt - 4;
-  for (int i = 1; i <= steady; ++i) {
-    mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
-    if (grp == 1) wait_vmem();
-    __syncthreads();
-    if (DEEP && grp == 0) wait_vmem();
-    const int j = i + ahead;
-    cp.k.issue(kh + (long long)(j * BN) * kss, ring.k(j), wave);
-    cp.v.issue(vh + (long long)((j - 1) * BN) * vss, ring.v(j - 1), wave);
-    valu_phase<T, TL, false, NEG, CAUSAL>(ws, i, klim, c, thr, sacc, pfr, lane);
-    if (!DEEP && grp == 0) wait_vmem();
-    __syncthreads();
+      if (!lead) wait_vmem();
+      __syncthreads();
+      if (DEEP && lead) wait_vmem();
+      const int j = i + ahead;
+      cp.k.issue(kh + (long long)(j * BN) * kss, ring.k(j), qw);
+      cp.v.issue(vh + (long long)((j - 1) * BN) * vss, ring.v(j - 1), qw);
+      valu_phase<T, TL, false, NEG, CAUSAL>(ws, i, klg, c, thr, sacc, pfr, lane);
+      if (!DEEP && lead) wait_vmem();
+      __syncthreads();
+    }
+    for (int i = steady + 1 > 1 ? steady + 1 : 1; i < ntg; ++i)
+      step(i, [&]() { copy_set(i + ahead); }, masked(i));
+    // Step ntg: P·V of the last tile.
+    mfma_phase<T, TL, false, true, NEG>(ws, nullptr, ring.v(ntg - 1), sacc, pfr, lane);
   }
-  for (int i = steady + 1 > 1 ? steady + 1 : 1; i < nt; ++i)
-    step(i, [&]() { copy_set(i + ahead); }, masked(i));
-  // Step nt: P·V of the last tile.
-  mfma_phase<T, TL, false, true, NEG>(ws, nullptr, ring.v(nt - 1), sacc, pfr, lane);
   if (grp == 0) __syncthreads();  // group 1 has one barrier fewer to go
   __syncthreads();
+  if (KSPLIT) {
+    // Group 1 may have one tile fewer (or none): it idles through the slots
+    // group 0 still needs, so both pass the same barriers.
+    for (int i = ntg; i < nt0; ++i) {
+      __syncthreads();
+      __syncthreads();
+    }
+    merge_key_halves<TL>(ws, smem, grp, qw, lane);
+    if (grp == 1) return;
+  }
 
   store_output<T, TL>(p, ws, sp * p.o_split + b * p.o_sb + h * p.o_sh,
-                     sp * p.lse_split + (long long)bh * p.Sq, qt, wave, lane);
+                     sp * p.lse_split + (long long)bh * p.Sq, qt, qw, lane);
 }
 
 
@@ -786,8 +909,9 @@ void attn_fwd_kernel(Params p) {
   const int lane = threadIdx.x & 63;
   const int G = gridDim.x;
   Copies<TL> cp;
-  cp.k.init(wave, lane, (uint32_t)p.k_ss * 2u);
-  cp.v.init(wave, lane, (uint32_t)p.v_ss * 2u);
+  const int cw = TL::KSPLIT ? (wave & 3) : wave;  // index among the waves sharing a K/V stream
+  cp.k.init(cw, lane, (uint32_t)p.k_ss * 2u);
+  cp.v.init(cw, lane, (uint32_t)p.v_ss * 2u);
   // Persistent loop over work items ("B200 Attention Kernel from Scratch to
   // Near-SOTA in 60 Diagrams", Chapter 14 - Persistent: a static grid-stride
   // assignment).  Workgroups are dispatched round-robin over the 8 XCDs, so

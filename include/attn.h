@@ -117,7 +117,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 
 /* Launch configuration the library would use (for reporting and benchmarks). */
 typedef struct attn_config {
-  int variant;            /* tile variant id */
+  int variant;            /* tile variant id (see attn_variant_info) */
   int block_m;            /* query rows per work item */
   int block_n;            /* keys per K/V tile */
   int waves;              /* 64-lane waves per workgroup */
@@ -135,11 +135,14 @@ int attn_get_config(int B, int H, int S, int D, int dtype,
                     const attn_fwd_options_t* opts, attn_config_t* out);
 
 /* Describes tile variant `index` (0-based, in [0, attn_variant_count())):
- * writes its id, head dim, dtype, block_m, block_n, waves and stages.
- * Host-only; touches no device. */
+ * writes its id, head dim, dtype, block_m, block_n, waves, stages and
+ * key_split (1: the workgroup's two groups of waves hold the same block_m
+ * query rows and each streams half of the keys, merging at the end; 0: every
+ * wave holds its own rows of one shared key stream).  Any output pointer may
+ * be NULL.  Host-only; touches no device. */
 int attn_variant_count(void);
 int attn_variant_info(int index, int* id, int* head_dim, int* dtype, int* block_m,
-                      int* block_n, int* waves, int* stages);
+                      int* block_n, int* waves, int* stages, int* key_split);
 
 /* ---- general layouts, KV ranges and split-KV --------------------------------- */
 
