@@ -35,6 +35,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef ATTN_SPLIT_SOFTMAX
+#define ATTN_SPLIT_SOFTMAX 1
+#endif
+
 namespace attn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -143,6 +147,9 @@ struct Tile {
   // Per-lane 16-byte chunks one wave hands over in the key-split merge: the
   // O accumulators, then (m, l) of each query block.
   static constexpr int XCH = QB * (D / 32) * 4 + 1;
+  // The first half of each tile's softmax runs inside its MFMA phase (see
+  // mma_phase).
+  static constexpr bool SPLIT_SM = ATTN_SPLIT_SOFTMAX != 0;
   // Waves per SIMD the register allocation targets.
   static constexpr int WPE = NW / 4;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile sizes");
@@ -609,6 +616,211 @@ __device__ __forceinline__ void valu_phase(WaveState<TL>& ws, int i, int klim, f
   if (any) rescale_o(ws, alpha);
 }
 
+// ---- split softmax: its first half rides in the MFMA phase --------------------
+//
+// With TL::SPLIT_SM, M(i) issues the Sᵀ MFMAs of tile i first and the P·V
+// MFMAs of tile i-1 after them.  Once Sᵀ is complete, the first half of the
+// softmax of tile i runs between the P·V MFMAs, in issue slots the MFMA phase
+// leaves idle: the row maximum, the threshold-guarded move of m, and
+// s·c - m (in place).  V(i) is left with exp2, the row sums, the packing of P
+// and the rescale of O, so the VALU phase shrinks by about a third.  The
+// arithmetic is the same as in the unsplit phases.
+
+template <class T, class TL, bool QK, bool PV, bool NEG, bool GUARD>
+__device__ __forceinline__ bool mma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
+                                          SAcc<TL>& sacc, const PFrag<TL>& pfr,
+                                          float (&alpha)[TL::QB], float (&mprev)[TL::QB],
+                                          float (&mu)[TL::QB], float c, float thr, int lane) {
+  constexpr int QB = TL::QB, NB = TL::BN / 32, DT = TL::D / 16, DB = TL::D / 32;
+  constexpr int NQ = QK ? NB * DT : 0;   // Sᵀ MFMAs (slots 0 .. NQ-1)
+  constexpr int NP = PV ? NB * 2 * DB : 0;  // P·V MFMAs (slots NQ .. NS-1)
+  constexpr int NS = NQ + NP;
+  constexpr int NV = NB * 16;            // scores per lane per 32-query block
+  static_assert(NS >= 1, "empty phase");
+
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  uint32_t ka = (uint32_t)(uintptr_t)kl + (uint32_t)((lane & 31) * TL::KS + (lane >> 5) * 16);
+  uint32_t va = (uint32_t)(uintptr_t)vl + (uint32_t)((16 * (g >> 1) + (li >> 2)) * TL::VS +
+                                                      (2 * (li & 1) + (g & 1)) * 16 +
+                                                      ((li >> 1) & 1) * 8);
+  if (QK) asm volatile("" : "+v"(ka));
+  if (PV) asm volatile("" : "+v"(va));
+  const lds_t* kbase = (const lds_t*)(uintptr_t)ka;
+  const lds_t* vbase = (const lds_t*)(uintptr_t)va;
+  // Operand of slot s: a K fragment for an Sᵀ MFMA (key block s % NB, head-dim
+  // step s / NB) or a V fragment for a P·V MFMA (as in pipe_step).
+  auto frag = [&](int s) -> u32x4_t {
+    if (s < NQ) return ld_lds16(kbase + (s % NB) * 32 * TL::KS + (s / NB) * 32);
+    const int i = s - NQ;
+    const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
+    const lds_t* pv0 = vbase + (nb * 32 + 8 * mm) * TL::VS + db * 64;
+    const u32x2_t lo = ld_lds_tr(pv0);
+    const u32x2_t hi = ld_lds_tr(pv0 + 4 * TL::VS);
+    const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+    return a;
+  };
+  constexpr int LD = 2;  // operands are read two slots ahead
+  u32x4_t fr[NS];
+#pragma unroll
+  for (int j = 0; j < LD && j < NS; ++j) fr[j] = frag(j);
+
+  // First half of the softmax of the new Sᵀ, as a list of units: NV/2 pairs
+  // folded into four running maxima per block, the exchange and rebase step,
+  // then NV in-place s·c - mu.  The maximum is taken over every key of the
+  // tile: a tile with masked keys redoes it in its softmax_tail (from
+  // s·c - mu and mprev), so only whole visible tiles rely on it.
+  constexpr float kInit = NEG ? __builtin_inff() : -__builtin_inff();
+  float m4[QB][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m4[qb][j] = kInit;
+  float nm[QB];
+  bool any = false;
+  constexpr int MAXU = QK ? QB * NV / 2 : 0;
+  constexpr int NU = QK ? MAXU + 1 + QB * NV : 0;
+  auto unit = [&](int u) {
+    if (u < MAXU) {
+      const int qb = u / (NV / 2), w = u % (NV / 2);
+      const float x0 = sacc[qb][(2 * w) / 16][(2 * w) % 16];
+      const float x1 = sacc[qb][(2 * w + 1) / 16][(2 * w + 1) % 16];
+      float& m = m4[qb][w & 3];
+      m = NEG ? fminf(fminf(m, x0), x1) : fmaxf(fmaxf(m, x0), x1);
+    } else if (u == MAXU) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mx = NEG ? fminf(fminf(m4[qb][0], m4[qb][1]), fminf(m4[qb][2], m4[qb][3]))
+                             : fmaxf(fmaxf(m4[qb][0], m4[qb][1]), fmaxf(m4[qb][2], m4[qb][3]));
+        const float tm = NEG ? lane_pair_min(mx) : lane_pair_max(mx);
+        const float mcand = tm * c;  // tile row maximum in log2 units
+        const float mold = ws.m[qb];
+        const bool rebase = (mold == -__builtin_inff()) || (mcand > mold + thr);
+        const float mnew = rebase ? mcand : mold;
+        // A row that has seen no valid key yet keeps m = -inf; it then
+        // measures p against 0 so that no (-inf) - (-inf) is formed.
+        const float mref = (GUARD && mnew == -__builtin_inff()) ? 0.f : mnew;
+        alpha[qb] = __builtin_amdgcn_exp2f(mold - mref);  // 1 if kept, 0 on the first tile
+        any = any || (__builtin_amdgcn_ballot_w64(rebase) != 0);
+        ws.m[qb] = mnew;
+        mprev[qb] = mold;
+        mu[qb] = mref;
+        nm[qb] = -mref;
+      }
+    } else {
+      const int k = u - MAXU - 1;
+      const int qb = k / NV, v = k % NV;
+      float y = __builtin_fmaf(sacc[qb][v / 16][v % 16], c, nm[qb]);
+      asm volatile("" : "+v"(y));  // keep it here, not sunk into the VALU phase
+      sacc[qb][v / 16][v % 16] = y;
+    }
+  };
+  // Units ride on the P·V slots from the third on, when the Sᵀ results have
+  // landed; without P·V (the first tile) they run after the Sᵀ MFMAs.
+  constexpr int FIRST = NQ + 2;
+  constexpr int SLOTS = NS - FIRST;
+  const f32x16_t zero = {};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s < NQ) {
+      const int nb = s % NB, t = s / NB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        sacc[qb][nb] = Mma<T>::mfma(fr[s], ws.qf[qb][t], t == 0 ? zero : sacc[qb][nb]);
+    } else {
+      const int i = s - NQ;
+      const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const u32x4_t b = {pfr[qb][nb][4 * mm + 0], pfr[qb][nb][4 * mm + 1],
+                           pfr[qb][nb][4 * mm + 2], pfr[qb][nb][4 * mm + 3]};
+        ws.o[qb][db] = Mma<T>::mfma(fr[s], b, ws.o[qb][db]);
+      }
+    }
+    if (s + LD < NS) fr[s + LD] = frag(s + LD);
+    if (SLOTS > 0 && s >= FIRST) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (FIRST + (u * SLOTS) / NU == s) unit(u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (SLOTS <= 0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) unit(u);
+  }
+  return any;
+}
+
+// Second half of the softmax of tile i; sacc holds x = s·c - mu.  A tile
+// with masked keys first redoes the first half over its visible keys only:
+// the row maximum max(x) + mu against the maximum before the tile (mprev),
+// the threshold-guarded move, and the shift to the new reference.  Then
+// p = 2^(x - shift) (0 for masked keys), row-sum partials in fp32, P rounded
+// and packed, l = l·alpha + Σp and, if any row of the wave moved its maximum,
+// O·alpha.  Issued as wide independent passes.
+template <class T, class TL, bool MASK, bool GUARD>
+__device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[TL::QB], bool any,
+                                             SAcc<TL>& sacc, PFrag<TL>& pfr,
+                                             const float (&mprev)[TL::QB],
+                                             const float (&mu)[TL::QB], int kb, int klim,
+                                             float thr, int lane) {
+  constexpr int QB = TL::QB, NV = TL::BN / 32 * 16;
+  float sh[QB];  // subtracted from x before exp2
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) sh[qb] = 0.f;
+  int lim = klim - (kb + 16 * (lane >> 5));
+  if (MASK) {
+    asm volatile("" : "+v"(lim));
+    any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m4[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float x = sacc[qb][v / 16][v % 16];
+        if ((v / 16) * 32 + (v % 16) >= lim) x = -__builtin_inff();
+        m4[v & 3] = fmaxf(m4[v & 3], x);
+      }
+      const float tx = lane_pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      const float mcand = tx + mu[qb];  // tile row maximum over visible keys, log2 units
+      const float mold = mprev[qb];
+      const bool rebase = (mold == -__builtin_inff()) || (mcand > mold + thr);
+      const float mnew = rebase ? mcand : mold;
+      const float mref = (GUARD && mnew == -__builtin_inff()) ? 0.f : mnew;
+      alpha[qb] = __builtin_amdgcn_exp2f(mold - mref);
+      any = any || (__builtin_amdgcn_ballot_w64(rebase) != 0);
+      ws.m[qb] = mnew;
+      sh[qb] = mref - mu[qb];
+    }
+  }
+  float e[QB][NV];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      e[qb][v] = __builtin_amdgcn_exp2f(MASK ? sacc[qb][v / 16][v % 16] - sh[qb]
+                                             : sacc[qb][v / 16][v % 16]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (MASK) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        if ((v / 16) * 32 + (v % 16) >= lim) e[qb][v] = 0.f;
+    }
+    float l4[4] = {e[qb][0], e[qb][1], e[qb][2], e[qb][3]};
+#pragma unroll
+    for (int v = 4; v < NV; ++v) l4[v & 3] += e[qb][v];
+    ws.l[qb] = ws.l[qb] * alpha[qb] + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
+#pragma unroll
+    for (int w = 0; w < NV / 2; ++w)
+      pfr[qb][w / 8][w % 8] = Mma<T>::pack(e[qb][2 * w], e[qb][2 * w + 1]);
+  }
+  // O has received P·V of tile i-1 and not yet that of tile i.
+  if (any) rescale_o(ws, alpha);
+}
+
 // Key-split merge: group 1 hands its (m, l, O) to the wave of group 0 that
 // holds the same query rows, through LDS (the rings are idle at this point),
 // and group 0 combines the two partial results of each row:
@@ -839,23 +1051,44 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     if (!lead && !DEEP) copy_set(1);
     __syncthreads();
   }
+  // Softmax state handed from M(i) to V(i): rescale factors, the maximum
+  // before tile i and the reference the scores were shifted by.
+  float alpha[QB], mprev[QB], mu[QB];
+  bool any = false;
+  // M(i): P·V of tile i-1 (unless i == 0) and Sᵀ of tile i (unless i == ntg);
+  // V(i): softmax of tile i, masked (MK) when it is not a whole tile visible
+  // to every row.  With SPLIT_SM the softmax is shared between the two.
+#define ATTN_MPHASE(I, QK, PV)                                                                     \
+  do {                                                                                             \
+    if constexpr (TL::SPLIT_SM) {                                                                  \
+      const bool a_ = mma_phase<T, TL, QK, PV, NEG, CAUSAL>(                                      \
+          ws, QK ? ring.k(I) : nullptr, PV ? ring.v((I) - 1) : nullptr, sacc, pfr, alpha, mprev,   \
+          mu, c, thr, lane);                                                                       \
+      if (QK) any = a_;                                                                            \
+    } else {                                                                                       \
+      mfma_phase<T, TL, QK, PV, NEG>(ws, QK ? ring.k(I) : nullptr, PV ? ring.v((I) - 1) : nullptr, \
+                                     sacc, pfr, lane);                                             \
+    }                                                                                              \
+  } while (0)
+#define ATTN_VPHASE(I, MK)                                                                         \
+  do {                                                                                             \
+    if constexpr (TL::SPLIT_SM)                                                                    \
+      softmax_tail<T, TL, MK, CAUSAL>(ws, alpha, any, sacc, pfr, mprev, mu, (I) * BN, klg, thr,    \
+                                      lane);                                                       \
+    else                                                                                           \
+      valu_phase<T, TL, MK, NEG, CAUSAL>(ws, I, klg, c, thr, sacc, pfr, lane);                     \
+  } while (0)
   if (ntg > 0) {
-    // One step i: M(i) (P·V of tile i-1 unless i == 0, Sᵀ of tile i), then
-    // V(i) (softmax of tile i, masked when it is not a whole tile visible to
-    // every row).  `cset` issues the step's copies.
+    // One step i: M(i), then V(i).  `cset` issues the step's copies.
     auto step = [&](int i, auto cset, bool masked) {
-      if (i == 0)
-        mfma_phase<T, TL, true, false, NEG>(ws, ring.k(0), nullptr, sacc, pfr, lane);
-      else
-        mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
+      if (i == 0) ATTN_MPHASE(0, true, false);
+      else ATTN_MPHASE(i, true, true);
       if (!lead) wait_vmem();
       __syncthreads();
       if (DEEP && lead) wait_vmem();
       cset();
-      if (masked)
-        valu_phase<T, TL, true, NEG, CAUSAL>(ws, i, klg, c, thr, sacc, pfr, lane);
-      else
-        valu_phase<T, TL, false, NEG, CAUSAL>(ws, i, klg, c, thr, sacc, pfr, lane);
+      if (masked) ATTN_VPHASE(i, true);
+      else ATTN_VPHASE(i, false);
       if (!DEEP && lead) wait_vmem();
       __syncthreads();
     };
@@ -866,21 +1099,21 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     // carries no such branches.
     const int steady = CAUSAL ? min(ntg - 4, t_mask - tb - 1) : ntg - 4;
     for (int i = 1; i <= steady; ++i) {
-      mfma_phase<T, TL, true, true, NEG>(ws, ring.k(i), ring.v(i - 1), sacc, pfr, lane);
+      ATTN_MPHASE(i, true, true);
       if (!lead) wait_vmem();
       __syncthreads();
       if (DEEP && lead) wait_vmem();
       const int j = i + ahead;
       cp.k.issue(kh + (long long)(j * BN) * kss, ring.k(j), qw);
       cp.v.issue(vh + (long long)((j - 1) * BN) * vss, ring.v(j - 1), qw);
-      valu_phase<T, TL, false, NEG, CAUSAL>(ws, i, klg, c, thr, sacc, pfr, lane);
+      ATTN_VPHASE(i, false);
       if (!DEEP && lead) wait_vmem();
       __syncthreads();
     }
     for (int i = steady + 1 > 1 ? steady + 1 : 1; i < ntg; ++i)
       step(i, [&]() { copy_set(i + ahead); }, masked(i));
     // Step ntg: P·V of the last tile.
-    mfma_phase<T, TL, false, true, NEG>(ws, nullptr, ring.v(ntg - 1), sacc, pfr, lane);
+    ATTN_MPHASE(ntg, false, true);
   }
   if (grp == 0) __syncthreads();  // group 1 has one barrier fewer to go
   __syncthreads();
@@ -898,6 +1131,8 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   store_output<T, TL>(p, ws, sp * p.o_split + b * p.o_sb + h * p.o_sh,
                      sp * p.lse_split + (long long)bh * p.Sq, qt, qw, lane);
 }
+#undef ATTN_MPHASE
+#undef ATTN_VPHASE
 
 
 template <class T, class TL, bool NEG, bool CAUSAL>
