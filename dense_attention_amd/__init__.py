@@ -86,7 +86,7 @@ def load_library(path: str | None = None):
         lib.attn_variant_count.argtypes = []
         lib.attn_variant_count.restype = i
         ip = ctypes.POINTER(ctypes.c_int)
-        lib.attn_variant_info.argtypes = [i, ip, ip, ip, ip, ip, ip, ip, ip]
+        lib.attn_variant_info.argtypes = [i, ip, ip, ip, ip, ip, ip, ip, ip, ip]
         lib.attn_variant_info.restype = i
         lp = ctypes.POINTER(attn_layout)
         op = ctypes.POINTER(attn_fwd_options)
@@ -218,9 +218,10 @@ def attn_variants() -> list:
     lib = load_library()
     out = []
     for idx in range(lib.attn_variant_count()):
-        vals = [ctypes.c_int() for _ in range(8)]
+        vals = [ctypes.c_int() for _ in range(9)]
         _check(lib, lib.attn_variant_info(idx, *[ctypes.byref(x) for x in vals]))
-        keys = ["id", "head_dim", "dtype", "block_m", "block_n", "waves", "stages", "key_split"]
+        keys = ["id", "head_dim", "dtype", "block_m", "block_n", "waves", "stages", "key_split",
+                "soft_exp"]
         out.append({kk: x.value for kk, x in zip(keys, vals)})
     return out
 

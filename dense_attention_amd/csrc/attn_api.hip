@@ -68,6 +68,7 @@ struct Variant {
   int stages;
   int lds_bytes;
   int key_split;
+  int soft_exp;
   launch_fn launch;
   occ_fn occupancy;
 };
@@ -75,8 +76,12 @@ struct Variant {
 template <class T, int DTYPE, class TL>
 constexpr Variant make_variant(int id) {
   return Variant{id, DTYPE, TL::D, TL::BM, TL::BN, TL::NW, TL::STAGES, TL::LDS_BYTES,
-                 TL::KSPLIT ? 1 : 0, &launch_impl<T, TL>, &occupancy_impl<T, TL>};
+                 TL::KSPLIT ? 1 : 0, TL::POLY, &launch_impl<T, TL>, &occupancy_impl<T, TL>};
 }
+
+#ifndef ATTN_POLY_EVERY
+#define ATTN_POLY_EVERY 4
+#endif
 
 // Tile variants; ids are stable.  8 waves (256 query rows, two groups sharing
 // one K/V stream), 4 waves (128 rows, one wave per SIMD), and 8 waves with a
@@ -94,6 +99,11 @@ const Variant kVariants[] = {
     make_variant<F16, ATTN_F16, Tile<64, 64, 8, 1, true>>(10),
     make_variant<BF16, ATTN_BF16, Tile<128, 64, 8, 1, true>>(11),
     make_variant<F16, ATTN_F16, Tile<128, 64, 8, 1, true>>(12),
+    // Software exp2 for one score in four (selectable, never the default).
+    make_variant<BF16, ATTN_BF16, Tile<64, 64, 8, 1, true, ATTN_POLY_EVERY>>(13),
+    make_variant<F16, ATTN_F16, Tile<64, 64, 8, 1, true, ATTN_POLY_EVERY>>(14),
+    make_variant<BF16, ATTN_BF16, Tile<128, 64, 8, 1, false, ATTN_POLY_EVERY>>(15),
+    make_variant<F16, ATTN_F16, Tile<128, 64, 8, 1, false, ATTN_POLY_EVERY>>(16),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -538,7 +548,7 @@ int attn_get_config(int B, int H, int S, int D, int dtype, const attn_fwd_option
 int attn_variant_count(void) { return kNumVariants; }
 
 int attn_variant_info(int index, int* id, int* head_dim, int* dtype, int* block_m, int* block_n,
-                      int* waves, int* stages, int* key_split) {
+                      int* waves, int* stages, int* key_split, int* soft_exp) {
   if (index < 0 || index >= kNumVariants) return fail(ATTN_ERR_ARG, "variant index out of range");
   const Variant& v = kVariants[index];
   if (id) *id = v.id;
@@ -549,6 +559,7 @@ int attn_variant_info(int index, int* id, int* head_dim, int* dtype, int* block_
   if (waves) *waves = v.waves;
   if (stages) *stages = v.stages;
   if (key_split) *key_split = v.key_split;
+  if (soft_exp) *soft_exp = v.soft_exp;
   return ATTN_OK;
 }
 

@@ -124,13 +124,16 @@ __device__ __forceinline__ int lane_key(int r) {
 // item.  This keeps two waves on every SIMD (the ping-pong below) with
 // 128-row work items, for problems with too few 256-row items to fill the
 // device.
-template <int D_, int BN_, int NW_, int QB_, bool KSPLIT_ = false>
+// POLY: when > 0, one score in every POLY of a tile gets 2^x from a cubic
+// polynomial on the VALU instead of v_exp_f32 (exp2_poly).
+template <int D_, int BN_, int NW_, int QB_, bool KSPLIT_ = false, int POLY_ = 0>
 struct Tile {
   static constexpr int D = D_;
   static constexpr int BN = BN_;            // keys per K/V tile
   static constexpr int NW = NW_;            // waves per workgroup
   static constexpr int QB = QB_;            // 32-query blocks per wave
   static constexpr bool KSPLIT = KSPLIT_;
+  static constexpr int POLY = POLY_;
   static constexpr int GW = KSPLIT ? NW / 2 : NW;  // waves sharing one K/V stream
   static constexpr int NT = NW * 64;        // threads per workgroup
   static constexpr int BM = GW * QB * 32;   // query rows per work item
@@ -501,6 +504,27 @@ __device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, co
   return any;
 }
 
+// 2^x without the transcendental unit: 2^x = 2^n · 2^f with n = floor(x),
+// f = x - n in [0, 1), and 2^f from a cubic whose coefficients minimise the
+// maximum relative error on [0, 1) with the constant term pinned to 1
+// (fit_exp2_poly.py, Remez exchange; max relative error 8.6e-5, below the
+// rounding of P to bf16 or fp16).  The selective use of a polynomial for part
+// of the exponentials is the B200 page's software exp2 (Chapter 9); the
+// coefficients here are fitted independently.  x below -127 is clamped there
+// (2^-127 is far below any P that survives the rounding to 16 bits).
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = fmaxf(x, -127.f);
+  // n from floor, not x - fract(x): fract saturates just below 1 for x just
+  // below an integer, and x - fract(x) is then not an integer.  f = x - n may
+  // round up to 1.0, where the cubic gives 2 - 1.4e-4: still 2^x.
+  const float n = __builtin_floorf(x);
+  const float f = x - n;
+  float p = __builtin_fmaf(0.077067042f, f, 0.227644991f);
+  p = __builtin_fmaf(p, f, 0.695116786f);
+  p = __builtin_fmaf(p, f, 1.0f);
+  return __builtin_amdgcn_ldexpf(p, (int)n);
+}
+
 template <class TL>
 __device__ __forceinline__ void rescale_o(WaveState<TL>& ws, const float (&alpha)[TL::QB]) {
 #pragma unroll
@@ -798,9 +822,11 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-      e[qb][v] = __builtin_amdgcn_exp2f(MASK ? sacc[qb][v / 16][v % 16] - sh[qb]
-                                             : sacc[qb][v / 16][v % 16]);
+    for (int v = 0; v < NV; ++v) {
+      const float x = MASK ? sacc[qb][v / 16][v % 16] - sh[qb] : sacc[qb][v / 16][v % 16];
+      e[qb][v] = (TL::POLY > 0 && v % (TL::POLY > 0 ? TL::POLY : 1) == 0) ? exp2_poly(x)
+                                                                           : __builtin_amdgcn_exp2f(x);
+    }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {

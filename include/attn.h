@@ -135,14 +135,18 @@ int attn_get_config(int B, int H, int S, int D, int dtype,
                     const attn_fwd_options_t* opts, attn_config_t* out);
 
 /* Describes tile variant `index` (0-based, in [0, attn_variant_count())):
- * writes its id, head dim, dtype, block_m, block_n, waves, stages and
+ * writes its id, head dim, dtype, block_m, block_n, waves, stages,
  * key_split (1: the workgroup's two groups of waves hold the same block_m
  * query rows and each streams half of the keys, merging at the end; 0: every
- * wave holds its own rows of one shared key stream).  Any output pointer may
- * be NULL.  Host-only; touches no device. */
+ * wave holds its own rows of one shared key stream) and soft_exp (0: every
+ * exponential on the transcendental unit; k > 0: one score in k takes 2^x
+ * from a cubic polynomial on the vector ALU, the selective software exp2 of
+ * "B200 Attention Kernel from Scratch to Near-SOTA in 60 Diagrams",
+ * Chapter 9; such variants are never the library's default).  Any output
+ * pointer may be NULL.  Host-only; touches no device. */
 int attn_variant_count(void);
 int attn_variant_info(int index, int* id, int* head_dim, int* dtype, int* block_m,
-                      int* block_n, int* waves, int* stages, int* key_split);
+                      int* block_n, int* waves, int* stages, int* key_split, int* soft_exp);
 
 /* ---- general layouts, KV ranges and split-KV --------------------------------- */
 

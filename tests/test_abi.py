@@ -129,13 +129,14 @@ def test_variant_table(lib):
         assert v["head_dim"] in (64, 128)
         assert v["dtype"] in (0, 1)
         assert v["key_split"] in (0, 1)
+        assert v["soft_exp"] >= 0
         rows_waves = v["waves"] // (2 if v["key_split"] else 1)
         assert v["block_m"] > 0 and v["block_m"] % (32 * rows_waves) == 0
         assert v["block_n"] % 64 == 0
     for d in (64, 128):
         for dt in (0, 1):
             assert any(v["head_dim"] == d and v["dtype"] == dt for v in vs)
-    assert lib.attn_variant_info(len(vs), None, None, None, None, None, None, None, None) == -8
+    assert lib.attn_variant_info(len(vs), None, None, None, None, None, None, None, None, None) == -8
 
 
 def test_strerror_covers_every_status(lib):

@@ -38,7 +38,8 @@ def _device():
 def split_variant(D, dtype):
     code = da.ATTN_F16 if dtype == "fp16" else da.ATTN_BF16
     ids = [v["id"] for v in da.attn_variants()
-           if v["head_dim"] == D and v["dtype"] == code and v["key_split"] == 1]
+           if v["head_dim"] == D and v["dtype"] == code and v["key_split"] == 1
+           and v["soft_exp"] == 0]
     assert len(ids) == 1, ids
     return ids[0]
 
