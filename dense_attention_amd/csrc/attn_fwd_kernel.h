@@ -35,10 +35,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#ifndef ATTN_SPLIT_SOFTMAX
-#define ATTN_SPLIT_SOFTMAX 1
-#endif
-
 namespace attn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -150,9 +146,6 @@ struct Tile {
   // Per-lane 16-byte chunks one wave hands over in the key-split merge: the
   // O accumulators, then (m, l) of each query block.
   static constexpr int XCH = QB * (D / 32) * 4 + 1;
-  // The first half of each tile's softmax runs inside its MFMA phase (see
-  // mma_phase).
-  static constexpr bool SPLIT_SM = ATTN_SPLIT_SOFTMAX != 0;
   // Waves per SIMD the register allocation targets.
   static constexpr int WPE = NW / 4;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile sizes");
@@ -299,210 +292,15 @@ struct WaveState {
   float l[TL::QB];                       // lane-partial row sum relative to m
 };
 
-// ---- work of one tile step ------------------------------------------------------
+// ---- register tiles ----------------------------------------------------------------
 //
-// pipe_step performs any combination of the three stages of a K/V tile:
-//   QK: Sᵀ = K·Qᵀ for the tile in `kl`,
-//   SM: online softmax of the scores in `s_in` (writes P to `p_out`),
-//   PV: Oᵀ += Vᵀ·Pᵀ with the tile in `vl` and P from `p_in`.
-// The stages touch disjoint registers.  The work is laid out as R regions:
-// region r issues QK MFMA r and PV MFMA r together with the LDS reads of
-// their operands two regions ahead, so every MFMA finds its operands
-// loaded.  When the softmax runs alone it is issued as wide
-// independent passes (see below); when it runs beside MFMAs its slices are
-// spread over the regions and scheduling barriers keep them there.
+// Sᵀ accumulators of one tile (32 keys per block) and the packed 16-bit P
+// fragments made from them (the B operand of Oᵀ += Vᵀ·Pᵀ).
 
 template <class TL>
 using SAcc = f32x16_t[TL::QB][TL::BN / 32];
 template <class TL>
 using PFrag = uint32_t[TL::QB][TL::BN / 32][8];
-
-template <class T, class TL, bool QK, bool SM, bool MASK, bool NEG, bool PV, bool GUARD = false>
-__device__ __forceinline__ bool pipe_step(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
-                                          const SAcc<TL>& s_in, SAcc<TL>& s_out,
-                                          const PFrag<TL>& p_in, PFrag<TL>& p_out,
-                                          float (&alpha)[TL::QB], int kb, int klim, float c,
-                                          float thr, int lane) {
-  constexpr int QB = TL::QB, NB = TL::BN / 32, DT = TL::D / 16, DB = TL::D / 32;
-  constexpr int NQ = NB * DT;        // K fragments (QK MFMA groups) per tile
-  constexpr int NP = NB * 2 * DB;    // V fragments (PV MFMA groups) per tile
-  constexpr int R = NQ > NP ? NQ : NP;
-  constexpr int NV = NB * 16;        // scores per lane per 32-query block
-  constexpr int NPAIR = QB * NV / 2; // packed P words per lane
-  static_assert(R >= 3, "pipeline needs at least three regions");
-
-  // Per-lane LDS bases.  K rows are in MFMA-lane order; the V transpose read:
-  // lane group g = lane/16 covers key half g/2 and head-dim half g%2; inside
-  // the group, lane i reads key row i/4 and the 8-byte piece of head-dim
-  // columns chosen so that the result is lane_key-ordered.
-  // The two bases are made opaque once per step: every operand read is then
-  // base + immediate, instead of an address the compiler rebuilds from the
-  // (runtime) ring slot before each read.
-  const int g = lane >> 4;
-  const int li = lane & 15;
-  uint32_t ka = (uint32_t)(uintptr_t)kl + (uint32_t)((lane & 31) * TL::KS + (lane >> 5) * 16);
-  uint32_t va = (uint32_t)(uintptr_t)vl + (uint32_t)((16 * (g >> 1) + (li >> 2)) * TL::VS +
-                                                      (2 * (li & 1) + (g & 1)) * 16 +
-                                                      ((li >> 1) & 1) * 8);
-  if (QK) asm volatile("" : "+v"(ka));
-  if (PV) asm volatile("" : "+v"(va));
-  const lds_t* kbase = (const lds_t*)(uintptr_t)ka;
-  const lds_t* vbase = (const lds_t*)(uintptr_t)va;
-
-  // QK MFMA i works on key block i % NB and head-dim step i / NB, so
-  // consecutive QK MFMAs accumulate into different key blocks.
-  auto kfrag = [&](int i) -> u32x4_t {
-    return ld_lds16(kbase + (i % NB) * 32 * TL::KS + (i / NB) * 32);
-  };
-  auto vfrag = [&](int i) -> u32x4_t {
-    const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
-    const lds_t* pv0 = vbase + (nb * 32 + 8 * mm) * TL::VS + db * 64;
-    const u32x2_t lo = ld_lds_tr(pv0);
-    const u32x2_t hi = ld_lds_tr(pv0 + 4 * TL::VS);
-    const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-    return a;
-  };
-
-  // Operands are read KD (K) and VD (V) regions ahead of their MFMA: one
-  // region is one or two MFMAs (32-64 cycles), shorter than an LDS read.
-  constexpr int KD = 2, VD = 2;
-  u32x4_t kf[NQ];
-  u32x4_t vf[NP];
-  if (QK) {
-#pragma unroll
-    for (int j = 0; j < KD && j < NQ; ++j) kf[j] = kfrag(j);
-  }
-  if (PV) {
-#pragma unroll
-    for (int j = 0; j < VD && j < NP; ++j) vf[j] = vfrag(j);
-  }
-
-  // softmax state.  Keys below klim (this lane's limit, counted from the
-  // start of the key range) are valid: key kb + 16·hh + 32·nb + i of a tile
-  // is valid iff 32·nb + i < lim; lim is opaque so the compares stay inside
-  // the step.
-  int lim = klim - (kb + 16 * (lane >> 5));
-  if (MASK) asm volatile("" : "+v"(lim));
-  constexpr float kInit = NEG ? __builtin_inff() : -__builtin_inff();
-  float mx[QB], nm[QB], ls[QB][2];
-  bool any = false;
-  const f32x16_t zero = {};
-
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    // ---- MFMA work of region r ----
-    if (QK && r < NQ) {
-      const int nb = r % NB, t = r / NB;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        s_out[qb][nb] = Mma<T>::mfma(kf[r], ws.qf[qb][t], t == 0 ? zero : s_out[qb][nb]);
-      if (r + KD < NQ) kf[r + KD] = kfrag(r + KD);
-    }
-    if (PV && r < NP) {
-      const int nb = r / (2 * DB), mm = (r / DB) % 2, db = r % DB;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const u32x4_t b = {p_in[qb][nb][4 * mm + 0], p_in[qb][nb][4 * mm + 1],
-                           p_in[qb][nb][4 * mm + 2], p_in[qb][nb][4 * mm + 3]};
-        ws.o[qb][db] = Mma<T>::mfma(vf[r], b, ws.o[qb][db]);
-      }
-      if (r + VD < NP) vf[r + VD] = vfrag(r + VD);
-    }
-    // ---- softmax slice of region r ----
-    if (SM) {
-      if (r == 0) {
-        // Row maximum of the tile (4 independent chains per lane).
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float m4[4] = {kInit, kInit, kInit, kInit};
-#pragma unroll
-          for (int v = 0; v < NV; ++v) {
-            float x = s_in[qb][v / 16][v % 16];
-            if (MASK && (v / 16) * 32 + (v % 16) >= lim) x = kInit;
-            m4[v & 3] = NEG ? fminf(m4[v & 3], x) : fmaxf(m4[v & 3], x);
-          }
-          mx[qb] = NEG ? fminf(fminf(m4[0], m4[1]), fminf(m4[2], m4[3]))
-                       : fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        }
-      } else if (r == 1) {
-        // Exchange with the other lane half, threshold-guarded move of m.
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float tm = NEG ? lane_pair_min(mx[qb]) : lane_pair_max(mx[qb]);
-          const float mcand = tm * c;  // tile row maximum in log2 units
-          const float mold = ws.m[qb];
-          const bool rebase = (mold == -__builtin_inff()) || (mcand > mold + thr);
-          const float mnew = rebase ? mcand : mold;
-          // A row that has seen no valid key yet keeps m = -inf; it then
-          // measures p against 0 so that no (-inf) - (-inf) is formed.
-          const float mref = (GUARD && mnew == -__builtin_inff()) ? 0.f : mnew;
-          alpha[qb] = __builtin_amdgcn_exp2f(mold - mref);  // 1 if kept, 0 on the first tile
-          any = any || (__builtin_amdgcn_ballot_w64(rebase) != 0);
-          ws.m[qb] = mnew;
-          nm[qb] = -mref;
-          ls[qb][0] = 0.f;
-          ls[qb][1] = 0.f;
-        }
-      } else {
-        // p = 2^(s·c - m), row-sum partials in fp32, P rounded and packed.
-        if (!QK && !PV) {
-          // Softmax-only phase: a single wave of the SIMD issues it, so expose
-          // the most independent work: all FMAs, then all exp2, then the sums
-          // and the packing.
-          if (r == 2) {
-            float e[QB][NV];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-              for (int v = 0; v < NV; ++v)
-                e[qb][v] = __builtin_fmaf(s_in[qb][v / 16][v % 16], c, nm[qb]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-              for (int v = 0; v < NV; ++v) e[qb][v] = __builtin_amdgcn_exp2f(e[qb][v]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              float l4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int v = 0; v < NV; ++v) {
-                if (MASK && (v / 16) * 32 + (v % 16) >= lim) e[qb][v] = 0.f;
-                l4[v & 3] += e[qb][v];
-              }
-              ls[qb][0] = l4[0] + l4[1];
-              ls[qb][1] = l4[2] + l4[3];
-#pragma unroll
-              for (int w = 0; w < NV / 2; ++w)
-                p_out[qb][w / 8][w % 8] = Mma<T>::pack(e[qb][2 * w], e[qb][2 * w + 1]);
-            }
-          }
-        } else {
-#pragma unroll
-        for (int k = 0; k < NPAIR; ++k) {
-          if (2 + (k * (R - 2)) / NPAIR != r) continue;
-          const int qb = k / (NV / 2), w = k % (NV / 2), nb = w / 8, i = 2 * (w % 8);
-          float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[qb][nb][i], c, nm[qb]));
-          float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[qb][nb][i + 1], c, nm[qb]));
-          if (MASK && nb * 32 + i >= lim) e0 = 0.f;
-          if (MASK && nb * 32 + i + 1 >= lim) e1 = 0.f;
-          ls[qb][0] += e0;
-          ls[qb][1] += e1;
-          uint32_t pw = Mma<T>::pack(e0, e1);
-          asm volatile("" : "+v"(pw));  // keep the packing here, not sunk to the step's end
-          p_out[qb][nb][i / 2] = pw;
-        }
-        }
-        if (r == R - 1) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) ws.l[qb] = ws.l[qb] * alpha[qb] + (ls[qb][0] + ls[qb][1]);
-        }
-      }
-    }
-    if ((QK ? 1 : 0) + (SM ? 1 : 0) + (PV ? 1 : 0) > 1) __builtin_amdgcn_sched_barrier(0);
-  }
-  return any;
-}
 
 // 2^x without the transcendental unit: 2^x = 2^n · 2^f with n = floor(x),
 // f = x - n in [0, 1), and 2^f from a cubic whose coefficients minimise the
@@ -607,8 +405,9 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
 // ---- ping-pong schedule ------------------------------------------------------
 //
 // Every wave runs the same sequence of phases, separated by workgroup
-// barriers:  M(i) = P·V of tile i-1 then Sᵀ of tile i (MFMA),  V(i) = softmax
-// of tile i (VALU).  With 8 waves, waves w and w+4 share a SIMD; group 1
+// barriers:  M(i) = Sᵀ of tile i then P·V of tile i-1 (MFMA, with the first
+// half of tile i's softmax between the P·V MFMAs),  V(i) = the rest of the
+// softmax of tile i (VALU).  With 8 waves, waves w and w+4 share a SIMD; group 1
 // (waves 4-7) starts one barrier later than group 0, so on every SIMD one wave
 // keeps the MFMA unit busy while the other keeps the VALU busy:
 //     slot 2i:   group 0 M(i)     group 1 V(i-1)
@@ -622,33 +421,16 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
 // their LDS operand reads; the three-deep ring makes that legal (see
 // process_item).
 
-template <class T, class TL, bool QK, bool PV, bool NEG>
-__device__ __forceinline__ void mfma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
-                                           SAcc<TL>& sacc, PFrag<TL>& pfr, int lane) {
-  float alpha[TL::QB];
-  pipe_step<T, TL, QK, false, false, NEG, PV>(ws, kl, vl, sacc, sacc, pfr, pfr, alpha, 0, 0, 0.f,
-                                              0.f, lane);
-}
-
-template <class T, class TL, bool MASK, bool NEG, bool GUARD>
-__device__ __forceinline__ void valu_phase(WaveState<TL>& ws, int i, int klim, float c, float thr,
-                                           SAcc<TL>& sacc, PFrag<TL>& pfr, int lane) {
-  float alpha[TL::QB];
-  const bool any = pipe_step<T, TL, false, true, MASK, NEG, false, GUARD>(
-      ws, nullptr, nullptr, sacc, sacc, pfr, pfr, alpha, i * TL::BN, klim, c, thr, lane);
-  // O has received P·V of tile i-1 and not yet that of tile i.
-  if (any) rescale_o(ws, alpha);
-}
-
 // ---- split softmax: its first half rides in the MFMA phase --------------------
 //
-// With TL::SPLIT_SM, M(i) issues the Sᵀ MFMAs of tile i first and the P·V
-// MFMAs of tile i-1 after them.  Once Sᵀ is complete, the first half of the
+// M(i) issues the Sᵀ MFMAs of tile i first and the P·V MFMAs of tile i-1
+// after them.  Once Sᵀ is complete, the first half of the
 // softmax of tile i runs between the P·V MFMAs, in issue slots the MFMA phase
 // leaves idle: the row maximum, the threshold-guarded move of m, and
 // s·c - m (in place).  V(i) is left with exp2, the row sums, the packing of P
-// and the rescale of O, so the VALU phase shrinks by about a third.  The
-// arithmetic is the same as in the unsplit phases.
+// and the rescale of O.  The work is laid out as slots of one MFMA each;
+// operands are read from LDS two slots ahead, and scheduling barriers keep
+// every slot's work in place.
 
 template <class T, class TL, bool QK, bool PV, bool NEG, bool GUARD>
 __device__ __forceinline__ bool mma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
@@ -673,7 +455,10 @@ __device__ __forceinline__ bool mma_phase(WaveState<TL>& ws, const lds_t* kl, co
   const lds_t* kbase = (const lds_t*)(uintptr_t)ka;
   const lds_t* vbase = (const lds_t*)(uintptr_t)va;
   // Operand of slot s: a K fragment for an Sᵀ MFMA (key block s % NB, head-dim
-  // step s / NB) or a V fragment for a P·V MFMA (as in pipe_step).
+  // step s / NB) or a V fragment for a P·V MFMA: lane group g = lane/16
+  // covers key half g/2 and head-dim half g%2; inside the group, lane i reads
+  // key row i/4 and the 8-byte piece of head-dim columns chosen so that the
+  // transposed result is lane_key-ordered.
   auto frag = [&](int s) -> u32x4_t {
     if (s < NQ) return ld_lds16(kbase + (s % NB) * 32 * TL::KS + (s / NB) * 32);
     const int i = s - NQ;
@@ -1081,29 +866,18 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   // before tile i and the reference the scores were shifted by.
   float alpha[QB], mprev[QB], mu[QB];
   bool any = false;
-  // M(i): P·V of tile i-1 (unless i == 0) and Sᵀ of tile i (unless i == ntg);
-  // V(i): softmax of tile i, masked (MK) when it is not a whole tile visible
-  // to every row.  With SPLIT_SM the softmax is shared between the two.
+  // M(i): Sᵀ of tile i (unless i == ntg) and P·V of tile i-1 (unless i == 0),
+  // with the first half of tile i's softmax; V(i): the rest of the softmax of
+  // tile i, masked (MK) when it is not a whole tile visible to every row.
 #define ATTN_MPHASE(I, QK, PV)                                                                     \
   do {                                                                                             \
-    if constexpr (TL::SPLIT_SM) {                                                                  \
-      const bool a_ = mma_phase<T, TL, QK, PV, NEG, CAUSAL>(                                      \
-          ws, QK ? ring.k(I) : nullptr, PV ? ring.v((I) - 1) : nullptr, sacc, pfr, alpha, mprev,   \
-          mu, c, thr, lane);                                                                       \
-      if (QK) any = a_;                                                                            \
-    } else {                                                                                       \
-      mfma_phase<T, TL, QK, PV, NEG>(ws, QK ? ring.k(I) : nullptr, PV ? ring.v((I) - 1) : nullptr, \
-                                     sacc, pfr, lane);                                             \
-    }                                                                                              \
+    const bool a_ = mma_phase<T, TL, QK, PV, NEG, CAUSAL>(                                        \
+        ws, QK ? ring.k(I) : nullptr, PV ? ring.v((I) - 1) : nullptr, sacc, pfr, alpha, mprev, mu, \
+        c, thr, lane);                                                                             \
+    if (QK) any = a_;                                                                              \
   } while (0)
-#define ATTN_VPHASE(I, MK)                                                                         \
-  do {                                                                                             \
-    if constexpr (TL::SPLIT_SM)                                                                    \
-      softmax_tail<T, TL, MK, CAUSAL>(ws, alpha, any, sacc, pfr, mprev, mu, (I) * BN, klg, thr,    \
-                                      lane);                                                       \
-    else                                                                                           \
-      valu_phase<T, TL, MK, NEG, CAUSAL>(ws, I, klg, c, thr, sacc, pfr, lane);                     \
-  } while (0)
+#define ATTN_VPHASE(I, MK) \
+  softmax_tail<T, TL, MK, CAUSAL>(ws, alpha, any, sacc, pfr, mprev, mu, (I) * BN, klg, thr, lane)
   if (ntg > 0) {
     // One step i: M(i), then V(i).  `cset` issues the step's copies.
     auto step = [&](int i, auto cset, bool masked) {
