@@ -1,8 +1,8 @@
 // Fused dense attention forward for gfx950 (MI355X): device code.
 //
-// One workgroup processes work items (batch, head, query tile) in a persistent
-// loop; inside an item it holds its Q rows in registers and streams the K/V
-// tiles of the head through a double-buffered LDS ring, computing
+// One workgroup processes work items (batch, head, query tile, key range) in a
+// persistent loop; inside an item it holds its Q rows in registers and streams
+// the K/V tiles of the head through a two- or three-deep LDS ring, computing
 //   S = Q·Kᵀ on MFMA, an online softmax in base 2, and O += P·V on MFMA,
 // then O / rowsum and the natural-log LSE.  This is the loop of "B200
 // Attention Kernel from Scratch to Near-SOTA in 60 Diagrams", Chapter 1 ("ii.
