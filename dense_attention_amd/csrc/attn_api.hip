@@ -31,30 +31,22 @@ int fail(int status, const char* detail) {
   return status;
 }
 
-typedef hipError_t (*launch_fn)(const Params&, bool neg, bool causal, int grid, hipStream_t stream);
+typedef hipError_t (*launch_fn)(const Params&, bool causal, int grid, hipStream_t stream);
 typedef hipError_t (*occ_fn)(int* blocks_per_cu);
 
-// Negative score multipliers use a separate instantiation (the running
-// maximum of c·s is then taken over min(s)), and so do causal masks.
+// Causal masks use a separate instantiation.
 template <class T, class TL>
-hipError_t launch_impl(const Params& p, bool neg, bool causal, int grid, hipStream_t stream) {
-  if (causal) {
-    if (neg)
-      hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, true, true>), dim3(grid), dim3(TL::NT), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, false, true>), dim3(grid), dim3(TL::NT), 0, stream, p);
-  } else {
-    if (neg)
-      hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, true, false>), dim3(grid), dim3(TL::NT), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, false, false>), dim3(grid), dim3(TL::NT), 0, stream, p);
-  }
+hipError_t launch_impl(const Params& p, bool causal, int grid, hipStream_t stream) {
+  if (causal)
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, true>), dim3(grid), dim3(TL::NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<T, TL, false>), dim3(grid), dim3(TL::NT), 0, stream, p);
   return hipGetLastError();
 }
 
 template <class T, class TL>
 hipError_t occupancy_impl(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attn::attn_fwd_kernel<T, TL, false, false>,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attn::attn_fwd_kernel<T, TL, false>,
                                                        TL::NT, 0);
 }
 
@@ -334,7 +326,7 @@ int launch_forward(const Forward& f, const Plan& plan, hipStream_t stream) {
   p.coff = plan.coff;
   p.c = f.scale * kLog2e;
   p.thr = plan.thr;
-  hipError_t e = plan.var->launch(p, p.c < 0.0f, plan.causal != 0, plan.grid, stream);
+  hipError_t e = plan.var->launch(p, plan.causal != 0, plan.grid, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, hipGetErrorString(e));
   return ATTN_OK;
 }

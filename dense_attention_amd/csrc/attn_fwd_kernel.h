@@ -432,11 +432,11 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
 // operands are read from LDS two slots ahead, and scheduling barriers keep
 // every slot's work in place.
 
-template <class T, class TL, bool QK, bool PV, bool NEG, bool GUARD>
-__device__ __forceinline__ bool mma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
+template <class T, class TL, bool QK, bool PV>
+__device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
                                           SAcc<TL>& sacc, const PFrag<TL>& pfr,
-                                          float (&alpha)[TL::QB], float (&mprev)[TL::QB],
-                                          float (&mu)[TL::QB], float c, float thr, int lane) {
+                                          float (&mprev)[TL::QB], float (&mu)[TL::QB], float c,
+                                          int lane) {
   constexpr int QB = TL::QB, NB = TL::BN / 32, DT = TL::D / 16, DB = TL::D / 32;
   constexpr int NQ = QK ? NB * DT : 0;   // Sᵀ MFMAs (slots 0 .. NQ-1)
   constexpr int NP = PV ? NB * 2 * DB : 0;  // P·V MFMAs (slots NQ .. NS-1)
@@ -474,55 +474,26 @@ __device__ __forceinline__ bool mma_phase(WaveState<TL>& ws, const lds_t* kl, co
 #pragma unroll
   for (int j = 0; j < LD && j < NS; ++j) fr[j] = frag(j);
 
-  // First half of the softmax of the new Sᵀ, as a list of units: NV/2 pairs
-  // folded into four running maxima per block, the exchange and rebase step,
-  // then NV in-place s·c - mu.  The maximum is taken over every key of the
-  // tile: a tile with masked keys redoes it in its softmax_tail (from
-  // s·c - mu and mprev), so only whole visible tiles rely on it.
-  constexpr float kInit = NEG ? __builtin_inff() : -__builtin_inff();
-  float m4[QB][4];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m4[qb][j] = kInit;
+  // First half of the softmax of the new Sᵀ: x = s·c - mu in place, one unit
+  // per score.  mu is the kept maximum m (0 while m is still -inf, so that no
+  // (-inf) - (-inf) is formed); mprev keeps m for softmax_tail, which decides
+  // whether the maximum moves.
   float nm[QB];
-  bool any = false;
-  constexpr int MAXU = QK ? QB * NV / 2 : 0;
-  constexpr int NU = QK ? MAXU + 1 + QB * NV : 0;
-  auto unit = [&](int u) {
-    if (u < MAXU) {
-      const int qb = u / (NV / 2), w = u % (NV / 2);
-      const float x0 = sacc[qb][(2 * w) / 16][(2 * w) % 16];
-      const float x1 = sacc[qb][(2 * w + 1) / 16][(2 * w + 1) % 16];
-      float& m = m4[qb][w & 3];
-      m = NEG ? fminf(fminf(m, x0), x1) : fmaxf(fmaxf(m, x0), x1);
-    } else if (u == MAXU) {
+  if (QK) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mx = NEG ? fminf(fminf(m4[qb][0], m4[qb][1]), fminf(m4[qb][2], m4[qb][3]))
-                             : fmaxf(fmaxf(m4[qb][0], m4[qb][1]), fmaxf(m4[qb][2], m4[qb][3]));
-        const float tm = NEG ? lane_pair_min(mx) : lane_pair_max(mx);
-        const float mcand = tm * c;  // tile row maximum in log2 units
-        const float mold = ws.m[qb];
-        const bool rebase = (mold == -__builtin_inff()) || (mcand > mold + thr);
-        const float mnew = rebase ? mcand : mold;
-        // A row that has seen no valid key yet keeps m = -inf; it then
-        // measures p against 0 so that no (-inf) - (-inf) is formed.
-        const float mref = (GUARD && mnew == -__builtin_inff()) ? 0.f : mnew;
-        alpha[qb] = __builtin_amdgcn_exp2f(mold - mref);  // 1 if kept, 0 on the first tile
-        any = any || (__builtin_amdgcn_ballot_w64(rebase) != 0);
-        ws.m[qb] = mnew;
-        mprev[qb] = mold;
-        mu[qb] = mref;
-        nm[qb] = -mref;
-      }
-    } else {
-      const int k = u - MAXU - 1;
-      const int qb = k / NV, v = k % NV;
-      float y = __builtin_fmaf(sacc[qb][v / 16][v % 16], c, nm[qb]);
-      asm volatile("" : "+v"(y));  // keep it here, not sunk into the VALU phase
-      sacc[qb][v / 16][v % 16] = y;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mold = ws.m[qb];
+      mprev[qb] = mold;
+      mu[qb] = mold == -__builtin_inff() ? 0.f : mold;
+      nm[qb] = -mu[qb];
     }
+  }
+  constexpr int NU = QK ? QB * NV : 0;
+  auto unit = [&](int k) {
+    const int qb = k / NV, v = k % NV;
+    float y = __builtin_fmaf(sacc[qb][v / 16][v % 16], c, nm[qb]);
+    asm volatile("" : "+v"(y));  // keep it here, not sunk into the VALU phase
+    sacc[qb][v / 16][v % 16] = y;
   };
   // Units ride on the P·V slots from the third on, when the Sᵀ results have
   // landed; without P·V (the first tile) they run after the Sᵀ MFMAs.
@@ -558,29 +529,69 @@ __device__ __forceinline__ bool mma_phase(WaveState<TL>& ws, const lds_t* kl, co
 #pragma unroll
     for (int u = 0; u < NU; ++u) unit(u);
   }
-  return any;
 }
 
-// Second half of the softmax of tile i; sacc holds x = s·c - mu.  A tile
-// with masked keys first redoes the first half over its visible keys only:
-// the row maximum max(x) + mu against the maximum before the tile (mprev),
-// the threshold-guarded move, and the shift to the new reference.  Then
-// p = 2^(x - shift) (0 for masked keys), row-sum partials in fp32, P rounded
-// and packed, l = l·alpha + Σp and, if any row of the wave moved its maximum,
-// O·alpha.  Issued as wide independent passes.
+// Second half of the softmax of tile i; sacc holds x = s·c - mu.
+//
+// The lazy rescale (reading of "B200 Attention Kernel from Scratch to
+// Near-SOTA in 60 Diagrams", Chapter 11) moves the kept maximum m only when a
+// tile's row maximum exceeds it by more than thr.  Instead of taking every
+// tile's maximum, p = 2^x is computed against the kept m first: a lane whose
+// partial row sum is at most 2^thr has every p <= 2^thr, so none of its scores
+// exceeds m + thr and its row keeps m.  Only when some lane of the wave fails
+// that test (or m is still -inf, or the tile has masked keys) does the wave
+// take the maxima: each row's maximum over its visible keys, max(x) + mu,
+// against m, the threshold-guarded move, the shift to the new reference, and
+// p again.  Rows that keep m get the same p either way.  Then the row-sum
+// partials in fp32, P rounded and packed, l = l·alpha + Σp and, if a row of
+// the wave moved its maximum, O·alpha.  Issued as wide independent passes.
 template <class T, class TL, bool MASK, bool GUARD>
-__device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[TL::QB], bool any,
+__device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[TL::QB], bool& any,
                                              SAcc<TL>& sacc, PFrag<TL>& pfr,
                                              const float (&mprev)[TL::QB],
                                              const float (&mu)[TL::QB], int kb, int klim,
-                                             float thr, int lane) {
+                                             float thr, float psum_max, int lane) {
   constexpr int QB = TL::QB, NV = TL::BN / 32 * 16;
-  float sh[QB];  // subtracted from x before exp2
+  int lim = klim - (kb + 16 * (lane >> 5));
+  if (MASK) asm volatile("" : "+v"(lim));
+  auto exp2_all = [&](float (&e)[QB][NV], const float (&sh)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const float x = sacc[qb][v / 16][v % 16] - sh[qb];
+        e[qb][v] = (TL::POLY > 0 && v % (TL::POLY > 0 ? TL::POLY : 1) == 0) ? exp2_poly(x)
+                                                                             : __builtin_amdgcn_exp2f(x);
+      }
+  };
+  auto row_sums = [&](float (&e)[QB][NV], float (&ls)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (MASK) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if ((v / 16) * 32 + (v % 16) >= lim) e[qb][v] = 0.f;
+      }
+      float l4[4] = {e[qb][0], e[qb][1], e[qb][2], e[qb][3]};
+#pragma unroll
+      for (int v = 4; v < NV; ++v) l4[v & 3] += e[qb][v];
+      ls[qb] = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    }
+  };
+  float e[QB][NV], ls[QB], sh[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) sh[qb] = 0.f;
-  int lim = klim - (kb + 16 * (lane >> 5));
-  if (MASK) {
-    asm volatile("" : "+v"(lim));
+  bool slow = MASK;
+  if (!MASK) {
+    exp2_all(e, sh);
+    __builtin_amdgcn_sched_barrier(0);
+    row_sums(e, ls);
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) need = need || (mprev[qb] == -__builtin_inff()) || !(ls[qb] <= psum_max);
+    slow = __builtin_amdgcn_ballot_w64(need) != 0;
+  }
+  if (slow) {
     any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -588,7 +599,7 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         float x = sacc[qb][v / 16][v % 16];
-        if ((v / 16) * 32 + (v % 16) >= lim) x = -__builtin_inff();
+        if (MASK && (v / 16) * 32 + (v % 16) >= lim) x = -__builtin_inff();
         m4[v & 3] = fmaxf(m4[v & 3], x);
       }
       const float tx = lane_pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
@@ -597,33 +608,22 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
       const bool rebase = (mold == -__builtin_inff()) || (mcand > mold + thr);
       const float mnew = rebase ? mcand : mold;
       const float mref = (GUARD && mnew == -__builtin_inff()) ? 0.f : mnew;
-      alpha[qb] = __builtin_amdgcn_exp2f(mold - mref);
+      alpha[qb] = __builtin_amdgcn_exp2f(mold - mref);  // 1 if kept, 0 on the first tile
       any = any || (__builtin_amdgcn_ballot_w64(rebase) != 0);
       ws.m[qb] = mnew;
       sh[qb] = mref - mu[qb];
     }
+    exp2_all(e, sh);
+    __builtin_amdgcn_sched_barrier(0);
+    row_sums(e, ls);
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) alpha[qb] = 1.f;
+    any = false;
   }
-  float e[QB][NV];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const float x = MASK ? sacc[qb][v / 16][v % 16] - sh[qb] : sacc[qb][v / 16][v % 16];
-      e[qb][v] = (TL::POLY > 0 && v % (TL::POLY > 0 ? TL::POLY : 1) == 0) ? exp2_poly(x)
-                                                                           : __builtin_amdgcn_exp2f(x);
-    }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    if (MASK) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-        if ((v / 16) * 32 + (v % 16) >= lim) e[qb][v] = 0.f;
-    }
-    float l4[4] = {e[qb][0], e[qb][1], e[qb][2], e[qb][3]};
-#pragma unroll
-    for (int v = 4; v < NV; ++v) l4[v & 3] += e[qb][v];
-    ws.l[qb] = ws.l[qb] * alpha[qb] + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
+    ws.l[qb] = ws.l[qb] * alpha[qb] + ls[qb];
 #pragma unroll
     for (int w = 0; w < NV / 2; ++w)
       pfr[qb][w / 8][w % 8] = Mma<T>::pack(e[qb][2 * w], e[qb][2 * w + 1]);
@@ -696,7 +696,7 @@ __device__ __forceinline__ void merge_key_halves(WaveState<TL>& ws, lds_t* smem,
   __syncthreads();
 }
 
-template <class T, class TL, bool NEG, bool CAUSAL>
+template <class T, class TL, bool CAUSAL>
 __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& cp, lds_t* smem,
                                              int item, int wave, int lane) {
   constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, DB = D / 32, DT = D / 16;
@@ -740,6 +740,9 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   int S = min(p.Skv - k0, p.split_len);
   asm volatile("" : "+s"(S));
   const float c = p.c, thr = p.thr;
+  // A lane's partial row sum of p = 2^(s·c - m) up to this bound proves that
+  // none of its scores exceeds m + thr (see softmax_tail).
+  const float psum_max = __builtin_amdgcn_exp2f(thr);
   const int kss = p.k_ss, vss = p.v_ss;
   const uint32_t krb = (uint32_t)kss * 2u, vrb = (uint32_t)vss * 2u;
 
@@ -870,14 +873,11 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   // with the first half of tile i's softmax; V(i): the rest of the softmax of
   // tile i, masked (MK) when it is not a whole tile visible to every row.
 #define ATTN_MPHASE(I, QK, PV)                                                                     \
-  do {                                                                                             \
-    const bool a_ = mma_phase<T, TL, QK, PV, NEG, CAUSAL>(                                        \
-        ws, QK ? ring.k(I) : nullptr, PV ? ring.v((I) - 1) : nullptr, sacc, pfr, alpha, mprev, mu, \
-        c, thr, lane);                                                                             \
-    if (QK) any = a_;                                                                              \
-  } while (0)
-#define ATTN_VPHASE(I, MK) \
-  softmax_tail<T, TL, MK, CAUSAL>(ws, alpha, any, sacc, pfr, mprev, mu, (I) * BN, klg, thr, lane)
+  mma_phase<T, TL, QK, PV>(ws, QK ? ring.k(I) : nullptr, PV ? ring.v((I) - 1) : nullptr, sacc, pfr, \
+                           mprev, mu, c, lane)
+#define ATTN_VPHASE(I, MK)                                                                         \
+  softmax_tail<T, TL, MK, CAUSAL>(ws, alpha, any, sacc, pfr, mprev, mu, (I) * BN, klg, thr,        \
+                                  psum_max, lane)
   if (ntg > 0) {
     // One step i: M(i), then V(i).  `cset` issues the step's copies.
     auto step = [&](int i, auto cset, bool masked) {
@@ -935,7 +935,7 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
 #undef ATTN_VPHASE
 
 
-template <class T, class TL, bool NEG, bool CAUSAL>
+template <class T, class TL, bool CAUSAL>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 void attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[TL::LDS_BYTES];
@@ -958,7 +958,7 @@ void attn_fwd_kernel(Params p) {
     if (base >= p.n_items) break;
     int item = base + (int)blockIdx.x;
     if (p.xcd_remap) item = base + (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
-    if (item < p.n_items) process_item<T, TL, NEG, CAUSAL>(p, cp, smem, item, wave, lane);
+    if (item < p.n_items) process_item<T, TL, CAUSAL>(p, cp, smem, item, wave, lane);
   }
 }
 
