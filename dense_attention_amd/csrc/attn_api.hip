@@ -77,7 +77,8 @@ constexpr Variant make_variant(int id) {
 
 // Tile variants; ids are stable.  8 waves (256 query rows, two groups sharing
 // one K/V stream), 4 waves (128 rows, one wave per SIMD), and 8 waves with a
-// key split (128 rows, each group streaming half of the keys).
+// key split (128 rows, each group streaming half of the keys); 64- or
+// 128-key tiles.
 const Variant kVariants[] = {
     make_variant<BF16, ATTN_BF16, Tile<128, 64, 8, 1>>(1),
     make_variant<F16, ATTN_F16, Tile<128, 64, 8, 1>>(2),
@@ -91,6 +92,10 @@ const Variant kVariants[] = {
     make_variant<F16, ATTN_F16, Tile<64, 64, 8, 1, true>>(10),
     make_variant<BF16, ATTN_BF16, Tile<128, 64, 8, 1, true>>(11),
     make_variant<F16, ATTN_F16, Tile<128, 64, 8, 1, true>>(12),
+    make_variant<BF16, ATTN_BF16, Tile<64, 128, 8, 1>>(17),
+    make_variant<F16, ATTN_F16, Tile<64, 128, 8, 1>>(18),
+    make_variant<BF16, ATTN_BF16, Tile<64, 128, 8, 1, true>>(19),
+    make_variant<F16, ATTN_F16, Tile<64, 128, 8, 1, true>>(20),
     // Software exp2 for one score in four (selectable, never the default).
     make_variant<BF16, ATTN_BF16, Tile<64, 64, 8, 1, true, ATTN_POLY_EVERY>>(13),
     make_variant<F16, ATTN_F16, Tile<64, 64, 8, 1, true, ATTN_POLY_EVERY>>(14),
@@ -110,8 +115,10 @@ const Variant* find_variant(int id) {
 // 128-row items take about half as long each.  Compared in rounds of one
 // workgroup per compute unit, with 10% for the key split's merge.
 const Variant* default_variant(int D, int dtype, int64_t BH, int Sq, int num_cus) {
-  const int shared_id = D == 128 ? (dtype == ATTN_BF16 ? 1 : 2) : (dtype == ATTN_BF16 ? 7 : 8);
-  const int split_id = D == 128 ? (dtype == ATTN_BF16 ? 11 : 12) : (dtype == ATTN_BF16 ? 9 : 10);
+  // D = 64: 128-key tiles (half the barriers and rescale tests per key; at
+  // D = 128 they do not fit the registers of two waves per SIMD).
+  const int shared_id = D == 128 ? (dtype == ATTN_BF16 ? 1 : 2) : (dtype == ATTN_BF16 ? 17 : 18);
+  const int split_id = D == 128 ? (dtype == ATTN_BF16 ? 11 : 12) : (dtype == ATTN_BF16 ? 19 : 20);
   const Variant* a = find_variant(shared_id);
   const Variant* k = find_variant(split_id);
   if (num_cus <= 0) num_cus = 256;

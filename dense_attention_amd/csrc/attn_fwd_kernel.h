@@ -22,7 +22,7 @@
 // Memory path: K and V tiles go from HBM straight into LDS
 // (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at base + 16·i,
 // so the LDS placement of every 16-byte chunk is chosen through the global
-// address each lane loads).  LDS rows are padded (K: +16 bytes, V: +64 bytes)
+// address each lane loads).  LDS rows are padded (K: +16 bytes, V: +64 or +48)
 // so that every LDS read is a per-lane base plus an immediate offset and no
 // two lanes of a 64-bank pass hit the same bank:
 //   * K rows are stored in MFMA-lane order (LDS row p of a 32-row block holds
@@ -134,11 +134,13 @@ struct Tile {
   static constexpr int NT = NW * 64;        // threads per workgroup
   static constexpr int BM = GW * QB * 32;   // query rows per work item
   static constexpr int DC = D / 8;          // 16-byte chunks per row
+  static constexpr int RINGS = KSPLIT ? 2 : 1;
   static constexpr int KS = D * 2 + 16;     // LDS row stride of K (bytes)
-  static constexpr int VS = D * 2 + 64;     // LDS row stride of V (bytes)
+  // LDS row stride of V (bytes): 64 bytes of padding, or 48 where two-deep
+  // rings would not fit in LDS otherwise.
+  static constexpr int VS = 2 * RINGS * BN * (KS + D * 2 + 64) <= 160 * 1024 ? D * 2 + 64 : D * 2 + 48;
   static constexpr int K_TILE = BN * KS;
   static constexpr int V_TILE = BN * VS;
-  static constexpr int RINGS = KSPLIT ? 2 : 1;
   // K/V ring depth: three tiles when they fit in LDS, else two.
   static constexpr int STAGES = 3 * RINGS * (BN * (KS + VS)) <= 160 * 1024 ? 3 : 2;
   static constexpr int RING_BYTES = STAGES * (K_TILE + V_TILE);
@@ -519,9 +521,11 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
     }
     if (s + LD < NS) fr[s + LD] = frag(s + LD);
     if (SLOTS > 0 && s >= FIRST) {
+      // Slot FIRST + j takes units u with floor(u·SLOTS/NU) == j.
+      const int j = s - FIRST;
+      const int u0 = (j * NU + SLOTS - 1) / SLOTS, u1 = ((j + 1) * NU + SLOTS - 1) / SLOTS;
 #pragma unroll
-      for (int u = 0; u < NU; ++u)
-        if (FIRST + (u * SLOTS) / NU == s) unit(u);
+      for (int u = u0; u < u1; ++u) unit(u);
     }
     __builtin_amdgcn_sched_barrier(0);
   }

@@ -35,13 +35,14 @@ def _device():
     torch.cuda.synchronize()
 
 
-def split_variant(D, dtype):
+def split_variants(D, dtype):
+    """Every key-split tiling for (D, dtype) with hardware exp2 (64- and 128-key tiles)."""
     code = da.ATTN_F16 if dtype == "fp16" else da.ATTN_BF16
     ids = [v["id"] for v in da.attn_variants()
            if v["head_dim"] == D and v["dtype"] == code and v["key_split"] == 1
            and v["soft_exp"] == 0]
-    assert len(ids) == 1, ids
-    return ids[0]
+    assert ids, (D, dtype)
+    return ids
 
 
 def compare(o, lse, ro, rl, tag):
@@ -74,15 +75,15 @@ LENGTHS = [1, 64, 65, 129, 192, 300, 320, 1000]
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_tile_counts_and_tails(D, dtype):
-    var = split_variant(D, dtype)
     for S in LENGTHS:
         q, k, v = W.gaussian_qkv(2, 3, S, D, dtype, seed=4000 + S)
         scale = 1.0 / math.sqrt(D)
         ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale)
-        say(f"key split S={S} D={D} {dtype} variant {var}")
-        o, lse = da.attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), scale=scale, variant=var)
-        torch.cuda.synchronize()
-        compare(o, lse, ro, rl, f"S={S} D={D} {dtype}")
+        for var in split_variants(D, dtype):
+            say(f"key split S={S} D={D} {dtype} variant {var}")
+            o, lse = da.attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), scale=scale, variant=var)
+            torch.cuda.synchronize()
+            compare(o, lse, ro, rl, f"S={S} D={D} {dtype} v{var}")
 
 
 @pytest.mark.parametrize("thr", [0.0, 8.0, 64.0])
@@ -90,65 +91,65 @@ def test_halves_with_far_apart_maxima(thr):
     """Keys 512-1023 scaled x4: the second half's running maximum lies far above
     the first half's, so the merge weights 2^(m_g - m) span many octaves."""
     q, k, v = W.forced_rebase_qkv()
-    var = split_variant(64, "bf16")
-    ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / 8)
-    o, lse = da.attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), scale=1 / 8, variant=var,
-                            rescale_threshold=thr)
-    torch.cuda.synchronize()
-    compare(o, lse, ro, rl, f"forced rebase thr={thr}")
-    # The same with the large keys in the first half instead.
     kf, vf = k.flip(2).contiguous(), v.flip(2).contiguous()
-    ro, rl = attention_forward(W.to_f64(q), W.to_f64(kf), W.to_f64(vf), 1 / 8)
-    o, lse = da.attn_fwd_ex(q.cuda(), kf.cuda(), vf.cuda(), scale=1 / 8, variant=var,
-                            rescale_threshold=thr)
-    torch.cuda.synchronize()
-    compare(o, lse, ro, rl, f"forced rebase flipped thr={thr}")
+    ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / 8)
+    rof, rlf = attention_forward(W.to_f64(q), W.to_f64(kf), W.to_f64(vf), 1 / 8)
+    for var in split_variants(64, "bf16"):
+        o, lse = da.attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), scale=1 / 8, variant=var,
+                                rescale_threshold=thr)
+        torch.cuda.synchronize()
+        compare(o, lse, ro, rl, f"forced rebase thr={thr} v{var}")
+        # The same with the large keys in the first half instead.
+        o, lse = da.attn_fwd_ex(q.cuda(), kf.cuda(), vf.cuda(), scale=1 / 8, variant=var,
+                                rescale_threshold=thr)
+        torch.cuda.synchronize()
+        compare(o, lse, rof, rlf, f"forced rebase flipped thr={thr} v{var}")
 
 
 @pytest.mark.parametrize("D,dtype", [(64, "fp16"), (128, "bf16")])
 def test_negative_scale_and_causal(D, dtype):
-    var = split_variant(D, dtype)
     q, k, v = W.gaussian_qkv(1, 2, 333, D, dtype, seed=4100)
-    ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), -0.1)
-    o, lse = da.attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), scale=-0.1, variant=var)
-    torch.cuda.synchronize()
-    compare(o, lse, ro, rl, "scale=-0.1")
-    for off in [0, -70, 200]:
-        ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / math.sqrt(D),
-                                   causal_offset=off)
-        o, lse = da.attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), variant=var,
-                                causal=True if off == 0 else off)
+    for var in split_variants(D, dtype):
+        ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), -0.1)
+        o, lse = da.attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), scale=-0.1, variant=var)
         torch.cuda.synchronize()
-        compare(o, lse, ro, rl, f"causal offset {off}")
+        compare(o, lse, ro, rl, f"scale=-0.1 v{var}")
+        for off in [0, -70, 200]:
+            ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / math.sqrt(D),
+                                       causal_offset=off)
+            o, lse = da.attn_fwd_ex(q.cuda(), k.cuda(), v.cuda(), variant=var,
+                                    causal=True if off == 0 else off)
+            torch.cuda.synchronize()
+            compare(o, lse, ro, rl, f"causal offset {off} v{var}")
 
 
 @pytest.mark.parametrize("D,dtype", [(64, "fp16"), (128, "bf16")])
 def test_with_kv_ranges_and_strided_layouts(D, dtype):
     """Key split inside each KV range of attn_fwd_split, and over BSHD views
     with Sq != Skv."""
-    var = split_variant(D, dtype)
     q, k, v = W.gaussian_qkv(1, 4, 1500, D, dtype, seed=4200)
     scale = 1.0 / math.sqrt(D)
     ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale)
-    for n in [2, 3]:
-        o, lse = da.attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), scale=scale, kv_splits=n,
-                                   variant=var)
-        torch.cuda.synchronize()
-        compare(o, lse, ro, rl, f"kv_splits={n}")
     qs = W.gaussian_qkv(1, 4, 211, D, dtype, seed=4201)[0]
     to_bshd = lambda t: t.transpose(1, 2).contiguous().cuda().transpose(1, 2)
-    ro, rl = attention_forward(W.to_f64(qs), W.to_f64(k), W.to_f64(v), scale)
-    o, lse = da.attn_fwd_strided(to_bshd(qs), to_bshd(k), to_bshd(v), scale=scale, variant=var)
-    torch.cuda.synchronize()
-    compare(o, lse, ro, rl, "bshd Sq=211 Skv=1500")
+    ros, rls = attention_forward(W.to_f64(qs), W.to_f64(k), W.to_f64(v), scale)
+    for var in split_variants(D, dtype):
+        for n in [2, 3]:
+            o, lse = da.attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), scale=scale, kv_splits=n,
+                                       variant=var)
+            torch.cuda.synchronize()
+            compare(o, lse, ro, rl, f"kv_splits={n} v{var}")
+        o, lse = da.attn_fwd_strided(to_bshd(qs), to_bshd(k), to_bshd(v), scale=scale, variant=var)
+        torch.cuda.synchronize()
+        compare(o, lse, ros, rls, f"bshd Sq=211 Skv=1500 v{var}")
 
 
 def test_grid_sizes_agree_bit_for_bit():
     q, k, v = W.gaussian_qkv(1, 3, 777, 64, "fp16", seed=4300)
-    var = split_variant(64, "fp16")
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    ref, ref_l = da.attn_fwd_ex(qd, kd, vd, variant=var)
-    for g in [1, 5, 8, 17]:
-        o, lse = da.attn_fwd_ex(qd, kd, vd, variant=var, grid=g)
-        torch.cuda.synchronize()
-        assert torch.equal(o, ref) and torch.equal(lse, ref_l), g
+    for var in split_variants(64, "fp16"):
+        ref, ref_l = da.attn_fwd_ex(qd, kd, vd, variant=var)
+        for g in [1, 5, 8, 17]:
+            o, lse = da.attn_fwd_ex(qd, kd, vd, variant=var, grid=g)
+            torch.cuda.synchronize()
+            assert torch.equal(o, ref) and torch.equal(lse, ref_l), (var, g)
