@@ -12,19 +12,23 @@
  *     o[b,h,i,:] = sum_j softmax_j(scale * q[b,h,i,:]·k[b,h,j,:]) * v[b,h,j,:]
  *     lse[b,h,i] = ln sum_j exp(scale * q[b,h,i,:]·k[b,h,j,:])
  *
- * non-causal, no mask or bias, the same sequence length S for queries and keys.
- * Computed tile by tile with an online softmax so the S×S score matrix never
- * reaches device memory; fp32 accumulation; O is rounded to the input dtype
- * with round-to-nearest-even, LSE is stored in fp32.
+ * attn_fwd: no mask or bias, the same sequence length S for queries and keys.
+ * attn_fwd_ex adds an optional causal mask (then the sums above run over the
+ * keys a row may see), attn_fwd_strided other layouts and key lengths, and
+ * attn_fwd_partial / attn_merge / attn_fwd_split key ranges.  Computed tile by
+ * tile with an online softmax so the S×S score matrix never reaches device
+ * memory; fp32 accumulation; O is rounded to the input dtype with
+ * round-to-nearest-even, LSE is stored in fp32.
  *
- * Layout: q, k, v, o are contiguous row-major [B, H, S, D] arrays of the same
- * dtype (D fastest, then S, then H, then B).  lse is a contiguous [B, H, S]
- * fp32 array.  All pointers are DEVICE pointers on the current HIP device.
+ * Layout (attn_fwd, attn_fwd_ex, attn_fwd_split): q, k, v, o are contiguous
+ * row-major [B, H, S, D] arrays of the same dtype (D fastest, then S, then H,
+ * then B).  lse is a contiguous [B, H, S] fp32 array.  All pointers are DEVICE
+ * pointers on the current HIP device.
  *
- * Ownership: the caller owns every buffer and the stream.  The library never
- * allocates, frees or synchronises, and keeps no pointer past the call.  Work
- * is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
- * default stream).
+ * Ownership: the caller owns every buffer (the split-KV workspace included)
+ * and the stream.  The library never allocates, frees or synchronises, and
+ * keeps no pointer past the call.  Work is enqueued asynchronously on `stream`
+ * (a hipStream_t; NULL means the default stream).
  *
  * Errors: every entry point returns ATTN_OK (0) or a negative attn_status.
  * Arguments are validated before anything is launched; on an error nothing is
