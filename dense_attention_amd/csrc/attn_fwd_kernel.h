@@ -820,9 +820,10 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     if (t >= 1 && t <= ntg) copy_v(t - 1);
   };
 
-  // Prologue: c(0) (and with a three-deep ring c(1)) in flight while Q is
-  // loaded into registers.
-  constexpr bool DEEP = TL::STAGES == 3;
+  // Prologue: c(0) (and with copies two tiles ahead, c(1)) in flight while Q
+  // is loaded into registers.  DEEP: copies run two tiles ahead, on three-deep
+  // rings and on every key-split ring (see below).
+  constexpr bool DEEP = TL::STAGES == 3 || TL::KSPLIT;
   if (ntg > 0) {
     copy_set(0);
     if (DEEP) copy_set(1);
@@ -855,12 +856,14 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   //  * three-deep ring: ahead = 2; the leading schedule waits at the start of
   //    V(i).  c(i+2) overwrites K_{i-1} and V_{i-2}, last read in M(i-1),
   //    two slots or more before V(i).
-  //  * two-deep ring: ahead = 1 for the leading schedule, which waits at the
-  //    end of V(i) (after its softmax), and 2 for group 1 of a shared stream.
-  //    c(i+1) issued in V(i) overwrites K_{i-1} and V_{i-2} (read in M(i-1),
-  //    which ends before V(i) of either group starts); c(i+2) issued by
-  //    group 1 of a shared stream in slot 2i+2 overwrites K_i and V_{i-1},
-  //    read in slots 2i and 2i+1.
+  //  * two-deep ring of one group (key split): as three-deep.  c(i+2) issued
+  //    in V(i) overwrites K_i and V_{i-1}, which only this group's M(i)
+  //    reads, and M(i) ends before V(i).
+  //  * two-deep shared ring: ahead = 1 for the leading schedule, which waits
+  //    at the end of V(i) (after its softmax), and 2 for group 1.  c(i+1)
+  //    issued in V(i) overwrites K_{i-1} and V_{i-2} (read in M(i-1), which
+  //    ends before V(i) of either group starts); c(i+2) issued by group 1 in
+  //    slot 2i+2 overwrites K_i and V_{i-1}, read in slots 2i and 2i+1.
   // No DMA is issued or awaited inside a leading MFMA phase.
   const int ahead = (DEEP || !lead) ? 2 : 1;
   SAcc<TL> sacc;
