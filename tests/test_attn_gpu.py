@@ -193,6 +193,27 @@ def test_forced_rebase_thresholds(thr):
     check_full(o, lse, q, k, v, 1 / math.sqrt(64), tag=f"threshold {thr}")
 
 
+@pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "bf16"), (64, "fp16")])
+def test_forced_rebase_all_variants(D, dtype):
+    """The rebase path past the first tile in every tiling: the second half of
+    the keys scaled x4 moves the row maxima mid-stream, and keys growing along
+    the sequence move them on every tile."""
+    q, k, v = W.forced_rebase_qkv(B=1, H=2, S=1000, D=D, dtype=dtype, seed=31)
+    ramp = W.gaussian_qkv(1, 2, 1000, D, dtype, seed=32)
+    qr = ramp[0]
+    kr = (ramp[1].float() * torch.linspace(0.25, 3.0, 1000).view(1, 1, -1, 1)).to(ramp[1].dtype)
+    vr = v  # uniform on (-1, 1): peaked rows keep |O| small
+    scale = 1 / math.sqrt(D)
+    for var in variants_for(D, dtype):
+        for thr in [0.0, 8.0]:
+            say(f"forced rebase D={D} {dtype} variant {var} thr {thr}")
+            o, lse = gpu_run(q, k, v, scale, variant=var, rescale_threshold=thr)
+            check_full(o, lse, q, k, v, scale, tag=f"forced v{var} thr {thr}")
+        say(f"growing keys D={D} {dtype} variant {var}")
+        o, lse = gpu_run(qr, kr, vr, scale, variant=var)
+        check_full(o, lse, qr, kr, vr, scale, tag=f"growing keys v{var}")
+
+
 def test_tile_signature_exact():
     """Q = 0 and a one-hot V per 64-key tile: every stale, skipped or doubled tile shows."""
     for D, dtype in [(128, "bf16"), (64, "fp16")]:
