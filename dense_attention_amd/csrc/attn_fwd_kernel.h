@@ -150,6 +150,14 @@ struct Tile {
   static constexpr int XCH = QB * (D / 32) * 4 + 1;
   // Waves per SIMD the register allocation targets.
   static constexpr int WPE = NW / 4;
+  // Shared K/V stream at D = 128: the MFMA phase runs at raised wave priority
+  // and the copy blocks of a tile are dealt to the waves round-robin (K blocks
+  // first, V blocks continuing where K left off), so every wave issues four
+  // or five.  Measured about 1% faster there, and slower on the key split.
+  static constexpr bool PRIO = !KSPLIT && D == 128;
+  // D = 64: the Sᵀ and P·V MFMAs of a phase alternate (measured faster there;
+  // at D = 128 the split softmax between the P·V MFMAs wins).
+  static constexpr bool ALT = D == 64;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile sizes");
   static_assert(K_TILE % 1024 == 0 && V_TILE % 1024 == 0, "tiles must be whole DMA blocks");
   static_assert(!KSPLIT || NW == 8, "a key split pairs two groups of four waves");
@@ -181,11 +189,17 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const lds
 // row p of each 32-row block receives key lane_key(p).  Pad slots are not
 // loaded.  The per-lane byte offsets do not depend on the tile, so they are
 // computed once per kernel and a full tile costs one address add per block.
-template <class TL, int STRIDE, bool LANE_ORDER>
+template <class TL, int STRIDE, bool LANE_ORDER, int ROT = 0>
 struct DmaPlan {
   static constexpr int SPR = STRIDE / 16;              // 16-byte slots per LDS row
   static constexpr int BLOCKS = TL::BN * SPR / 64;     // 1 KiB blocks per tile
   static constexpr int BPW = (BLOCKS + TL::GW - 1) / TL::GW;
+  // Block t of wave `wave`: contiguous runs of BPW blocks, or with PRIO dealt
+  // round-robin starting at wave ROT.
+  __device__ __forceinline__ static int block(int wave, int t) {
+    if (TL::PRIO) return (wave + TL::GW - ROT % TL::GW) % TL::GW + t * TL::GW;
+    return wave * BPW + t;
+  }
   // Byte offset of this lane's chunk from the tile's first row.  Pad slots load
   // chunk 0 of their row again (the pad bytes of an LDS row are never read).
   uint32_t off[BPW];
@@ -203,7 +217,7 @@ struct DmaPlan {
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
       int key, c;
-      slot_rc(wave * BPW + t, lane, key, c);
+      slot_rc(block(wave, t), lane, key, c);
       off[t] = (uint32_t)key * row_bytes + (uint32_t)c * 16u;
     }
   }
@@ -212,7 +226,7 @@ struct DmaPlan {
   __device__ __forceinline__ void issue(const uint16_t* tile, lds_t* dst, int wave) const {
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
-      const int blk = wave * BPW + t;
+      const int blk = block(wave, t);
       if (BLOCKS % TL::GW == 0 || blk < BLOCKS) {
         // Opaque per call: keeps the address as uniform base + 32-bit lane
         // offset instead of a hoisted 64-bit per-lane pointer.
@@ -229,7 +243,7 @@ struct DmaPlan {
                                                 lds_t* dst, int wave, int lane) const {
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
-      const int blk = wave * BPW + t;
+      const int blk = block(wave, t);
       if (BLOCKS % TL::GW == 0 || blk < BLOCKS) {
         int key, c;
         slot_rc(blk, lane, key, c);
@@ -349,7 +363,7 @@ struct Ring {
 template <class TL>
 struct Copies {
   DmaPlan<TL, TL::KS, true> k;
-  DmaPlan<TL, TL::VS, false> v;
+  DmaPlan<TL, TL::VS, false, (TL::BN * TL::KS / 1024) % TL::GW> v;
 };
 
 // Epilogue of a work item: O / l (rounded to the output type, or fp32 for a
@@ -461,9 +475,18 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
   // covers key half g/2 and head-dim half g%2; inside the group, lane i reads
   // key row i/4 and the 8-byte piece of head-dim columns chosen so that the
   // transposed result is lane_key-ordered.
+  // Slot order: all Sᵀ slots then all P·V slots, or with ALT (and both kinds
+  // present) Sᵀ in the even slots and P·V in the odd ones.
+  constexpr bool IL = TL::ALT && QK && PV && NQ == NP;
+  auto is_qk = [](int s) { return IL ? s % 2 == 0 : s < NQ; };
+  auto qk_index = [](int s) { return IL ? s / 2 : s; };
+  auto pv_index = [](int s) { return IL ? s / 2 : s - NQ; };
   auto frag = [&](int s) -> u32x4_t {
-    if (s < NQ) return ld_lds16(kbase + (s % NB) * 32 * TL::KS + (s / NB) * 32);
-    const int i = s - NQ;
+    if (is_qk(s)) {
+      const int q = qk_index(s);
+      return ld_lds16(kbase + (q % NB) * 32 * TL::KS + (q / NB) * 32);
+    }
+    const int i = pv_index(s);
     const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
     const lds_t* pv0 = vbase + (nb * 32 + 8 * mm) * TL::VS + db * 64;
     const u32x2_t lo = ld_lds_tr(pv0);
@@ -472,6 +495,7 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
     return a;
   };
   constexpr int LD = 2;  // operands are read two slots ahead
+  if (TL::PRIO) __builtin_amdgcn_s_setprio(3);
   u32x4_t fr[NS];
 #pragma unroll
   for (int j = 0; j < LD && j < NS; ++j) fr[j] = frag(j);
@@ -498,19 +522,21 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
     sacc[qb][v / 16][v % 16] = y;
   };
   // Units ride on the P·V slots from the third on, when the Sᵀ results have
-  // landed; without P·V (the first tile) they run after the Sᵀ MFMAs.
+  // landed; without P·V (the first tile), or with alternating slots, they run
+  // after the last MFMA.
   constexpr int FIRST = NQ + 2;
   constexpr int SLOTS = NS - FIRST;
   const f32x16_t zero = {};
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (s < NQ) {
-      const int nb = s % NB, t = s / NB;
+    if (is_qk(s)) {
+      const int q = qk_index(s);
+      const int nb = q % NB, t = q / NB;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         sacc[qb][nb] = Mma<T>::mfma(fr[s], ws.qf[qb][t], t == 0 ? zero : sacc[qb][nb]);
     } else {
-      const int i = s - NQ;
+      const int i = pv_index(s);
       const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -520,7 +546,7 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
       }
     }
     if (s + LD < NS) fr[s + LD] = frag(s + LD);
-    if (SLOTS > 0 && s >= FIRST) {
+    if (!IL && SLOTS > 0 && s >= FIRST) {
       // Slot FIRST + j takes units u with floor(u·SLOTS/NU) == j.
       const int j = s - FIRST;
       const int u0 = (j * NU + SLOTS - 1) / SLOTS, u1 = ((j + 1) * NU + SLOTS - 1) / SLOTS;
@@ -529,10 +555,11 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (SLOTS <= 0) {
+  if (IL || SLOTS <= 0) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) unit(u);
   }
+  if (TL::PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
 // Second half of the softmax of tile i; sacc holds x = s·c - mu.
