@@ -67,6 +67,13 @@ class attn_config(ctypes.Structure):
 def load_library(path: str | None = None):
     """Loads libattn.so (once).  Raises if it has not been built."""
     global _lib
+    # torch ships its own HIP runtime (libamdhip64.so.7).  Loaded first, it
+    # satisfies libattn.so's dependency of the same soname, so the library and
+    # torch share one runtime: the device, the streams and the pointers torch
+    # hands over are then the library's too.  Loaded after libattn.so, torch
+    # would map a second runtime next to ROCm's and the two would not see each
+    # other's device state.
+    import torch  # noqa: F401
     with _lock:
         if _lib is not None and path is None:
             return _lib

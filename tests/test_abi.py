@@ -6,6 +6,7 @@ import math
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -244,3 +245,22 @@ def test_causal_option_validation(lib):
     o = da._options(None, 0, 0, -7)
     assert (o.causal, o.causal_offset) == (2, -7)
     assert da._options(None, 0, 0, False).causal == 0
+
+
+def test_library_shares_torch_hip_runtime():
+    """Loading the library before torch must still leave one HIP runtime mapped.
+
+    A second libamdhip64 next to torch's own would keep its own device state,
+    so pointers and streams from torch would not be valid in the library.
+    """
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import dense_attention_amd as da\n"
+        "da.load_library()\n"
+        "import torch\n"
+        "maps = open('/proc/self/maps').read()\n"
+        "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n"
+    ) % os.path.dirname(os.path.dirname(os.path.abspath(da.__file__)))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
