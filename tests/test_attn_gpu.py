@@ -122,6 +122,48 @@ def test_config_hd128_bf16_sampled(idx):
     assert bool(((of >= lo - 1e-2) & (of <= hi + 1e-2)).all())
 
 
+def _check_sampled(w, q, k, v, go, gl, seed, tag):
+    qn, kn, vn = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (w.B - 1, w.H - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.H)))
+                                              for _ in range(2)}
+    worst_o = worst_l = 0.0
+    errs = []
+    for (b, h) in sorted(pairs):
+        rows = _sample_rows(w.S, 32, rng)
+        ro, rl = attention_rows(qn, kn, vn, w.scale, b, h, rows)
+        e = np.abs(go[b, h, rows].double().numpy() - ro)
+        errs.append(e)
+        worst_o = max(worst_o, e.max())
+        worst_l = max(worst_l, np.abs(gl[b, h, rows] - rl).max())
+    allerr = np.concatenate([e.ravel() for e in errs])
+    say(f"  {tag} sampled O max {worst_o:.3e} mean {allerr.mean():.3e} LSE max {worst_l:.3e}")
+    assert worst_o <= O_MAX and allerr.mean() <= O_MEAN and worst_l <= LSE_MAX, tag
+
+
+def test_bench_bshd_and_split_launches_sampled():
+    """The benchmark's other launch paths at the S = 8192, D = 128 size: BSHD
+    storage through attn_fwd_strided (``--layout bshd``) and split-KV with the
+    library's own range count (``--kv-splits 0``); sampled rows against the oracle."""
+    w = W.CONFIGS[3]
+    q, k, v = W.workload_qkv(w)
+    say(f"{w.name} BSHD storage through attn_fwd_strided")
+    qd, kd, vd = (t.transpose(1, 2).contiguous().cuda().transpose(1, 2) for t in (q, k, v))
+    od = torch.empty((w.B, w.S, w.H, w.D), dtype=q.dtype, device="cuda").transpose(1, 2)
+    o, lse = da.attn_fwd_strided(qd, kd, vd, od, scale=w.scale)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == od.data_ptr()
+    _check_sampled(w, q, k, v, o.cpu(), lse.cpu().double().numpy(), 200, "bshd")
+    del qd, kd, vd, od, o, lse
+    say(f"{w.name} split-KV, library range count")
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    nbytes = da.attn_fwd_split_workspace_size(w.B, w.H, w.S, w.D, 0)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    o, lse = da.attn_fwd_split(qd, kd, vd, scale=w.scale, kv_splits=0, workspace=ws)
+    torch.cuda.synchronize()
+    _check_sampled(w, q, k, v, o.cpu(), lse.cpu().double().numpy(), 201, "split")
+
+
 # --- edge cases -----------------------------------------------------------------
 
 RAGGED = [1, 2, 31, 64, 65, 100, 127, 129, 200, 257, 1000]
