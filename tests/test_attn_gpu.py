@@ -67,7 +67,7 @@ def variants_for(D, dtype):
 # --- the five workloads ------------------------------------------------------
 
 def test_config_small_fp16_all_variants():
-    w = W.CONFIGS[0]
+    w = W.BY_NAME["b1_h4_s128_d64_fp16"]
     q, k, v = W.workload_qkv(w)
     for var in [0] + variants_for(w.D, w.dtype):
         say(f"{w.name} variant {var}")
@@ -76,7 +76,7 @@ def test_config_small_fp16_all_variants():
 
 
 def test_config_s4096_d64_fp16_full():
-    w = W.CONFIGS[1]
+    w = W.BY_NAME["b1_h8_s4096_d64_fp16"]
     q, k, v = W.workload_qkv(w)
     say(f"{w.name} default launch")
     o, lse = gpu_run(q, k, v, w.scale)
@@ -89,9 +89,11 @@ def _sample_rows(S, n, rng, tile=128):
     return np.array(sorted(r for r in rows if 0 <= r < S))
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4], ids=lambda i: W.CONFIGS[i].name)
-def test_config_hd128_bf16_sampled(idx):
-    w = W.CONFIGS[idx]
+@pytest.mark.parametrize("name", ["b4_h16_s4096_d128_bf16", "b2_h16_s8192_d128_bf16",
+                                  "b1_h16_s16384_d128_bf16"])
+def test_config_hd128_bf16_sampled(name):
+    w = W.BY_NAME[name]
+    idx = W.WORKLOADS.index(w)
     q, k, v = W.workload_qkv(w)
     say(f"{w.name} default launch (the benchmark's)")
     o, lse = gpu_run(q, k, v, w.scale)
@@ -145,7 +147,7 @@ def test_bench_bshd_and_split_launches_sampled():
     """The benchmark's other launch paths at the S = 8192, D = 128 size: BSHD
     storage through attn_fwd_strided (``--layout bshd``) and split-KV with the
     library's own range count (``--kv-splits 0``); sampled rows against the oracle."""
-    w = W.CONFIGS[3]
+    w = W.BY_NAME["b2_h16_s8192_d128_bf16"]
     q, k, v = W.workload_qkv(w)
     say(f"{w.name} BSHD storage through attn_fwd_strided")
     qd, kd, vd = (t.transpose(1, 2).contiguous().cuda().transpose(1, 2) for t in (q, k, v))

@@ -67,14 +67,14 @@ class Workload:
 # The five problems: the small fp16 listing case and the fp16 benchmark case of
 # "Learning FlashAttention the Hard Way - Part 2" (SDPA_L, SDPA_P), and three
 # hd128 bf16 cases at S = 4K / 8K / 16K with 16384 tokens each.
-CONFIGS = [
+WORKLOADS = [
     Workload("b1_h4_s128_d64_fp16", 1, 4, 128, 64, "fp16", 1),
     Workload("b1_h8_s4096_d64_fp16", 1, 8, 4096, 64, "fp16", 2),
     Workload("b4_h16_s4096_d128_bf16", 4, 16, 4096, 128, "bf16", 3),
     Workload("b2_h16_s8192_d128_bf16", 2, 16, 8192, 128, "bf16", 4),
     Workload("b1_h16_s16384_d128_bf16", 1, 16, 16384, 128, "bf16", 5),
 ]
-BY_NAME = {w.name: w for w in CONFIGS}
+BY_NAME = {w.name: w for w in WORKLOADS}
 
 
 def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
