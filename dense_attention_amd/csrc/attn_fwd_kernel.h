@@ -299,6 +299,12 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// A compile-time integer carried through generic lambdas.
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 // Per-wave state of one work item.
 template <class TL>
 struct WaveState {
@@ -932,18 +938,44 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     // remaining (at least the last three) steps are peeled so the steady loop
     // carries no such branches.
     const int steady = CAUSAL ? min(ntg - 4, t_mask - tb - 1) : ntg - 4;
-    for (int i = 1; i <= steady; ++i) {
-      ATTN_MPHASE(i, true, true);
+    // Steady step i.  With copies two tiles ahead the loop is unrolled by the
+    // ring depth, so every ring buffer a step touches (K_i, V_{i-1}, and the
+    // copy targets K_{i+2}, V_{i+1}) is a compile-time offset: RR carries
+    // i % STAGES, or -1 where it is computed at run time.  This takes the
+    // modulo arithmetic and most address set-up out of the VALU phase.
+    auto steady_step = [&](int i, auto RR) {
+      constexpr int R = decltype(RR)::value;
+      constexpr int NS = TL::STAGES;
+      lds_t* const vbase = ring.base + NS * TL::K_TILE;
+      lds_t* const k_i = R >= 0 ? ring.base + R * TL::K_TILE : ring.k(i);
+      lds_t* const v_im1 = R >= 0 ? vbase + ((R + NS - 1) % NS) * TL::V_TILE : ring.v(i - 1);
+      mma_phase<T, TL, true, true>(ws, k_i, v_im1, sacc, pfr, mprev, mu, c, lane);
       if (!lead) wait_vmem();
       __syncthreads();
       if (DEEP && lead) wait_vmem();
       const int j = i + ahead;
-      cp.k.issue(kh + (long long)(j * BN) * kss, ring.k(j), qw);
-      cp.v.issue(vh + (long long)((j - 1) * BN) * vss, ring.v(j - 1), qw);
+      lds_t* const k_j = R >= 0 ? ring.base + ((R + 2) % NS) * TL::K_TILE : ring.k(j);
+      lds_t* const v_jm1 = R >= 0 ? vbase + ((R + 1) % NS) * TL::V_TILE : ring.v(j - 1);
+      cp.k.issue(kh + (long long)(j * BN) * kss, k_j, qw);
+      cp.v.issue(vh + (long long)((j - 1) * BN) * vss, v_jm1, qw);
       ATTN_VPHASE(i, false);
       if (!DEEP && lead) wait_vmem();
       __syncthreads();
+    };
+    int i0 = 1;
+    if (DEEP && TL::STAGES == 3) {
+      for (; i0 + 2 <= steady; i0 += 3) {
+        steady_step(i0, IntC<1>());
+        steady_step(i0 + 1, IntC<2>());
+        steady_step(i0 + 2, IntC<0>());
+      }
+    } else if (DEEP && TL::STAGES == 2) {
+      for (; i0 + 1 <= steady; i0 += 2) {
+        steady_step(i0, IntC<1>());
+        steady_step(i0 + 1, IntC<0>());
+      }
     }
+    for (int i = i0; i <= steady; ++i) steady_step(i, IntC<-1>());
     for (int i = steady + 1 > 1 ? steady + 1 : 1; i < ntg; ++i)
       step(i, [&]() { copy_set(i + ahead); }, masked(i));
     // Step ntg: P·V of the last tile.
