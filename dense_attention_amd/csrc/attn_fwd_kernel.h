@@ -454,7 +454,10 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
 // operands are read from LDS two slots ahead, and scheduling barriers keep
 // every slot's work in place.
 
-template <class T, class TL, bool QK, bool PV>
+// STEADY: a step of the steady loop, where every row's kept maximum is already
+// finite (tile 0 of the item, or of the group, was visible to every row), so
+// the guards for m = -inf are left out.
+template <class T, class TL, bool QK, bool PV, bool STEADY = false>
 __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
                                           SAcc<TL>& sacc, const PFrag<TL>& pfr,
                                           float (&mprev)[TL::QB], float (&mu)[TL::QB], float c,
@@ -516,7 +519,7 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
     for (int qb = 0; qb < QB; ++qb) {
       const float mold = ws.m[qb];
       mprev[qb] = mold;
-      mu[qb] = mold == -__builtin_inff() ? 0.f : mold;
+      mu[qb] = (!STEADY && mold == -__builtin_inff()) ? 0.f : mold;
       nm[qb] = -mu[qb];
     }
   }
@@ -582,7 +585,7 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
 // p again.  Rows that keep m get the same p either way.  Then the row-sum
 // partials in fp32, P rounded and packed, l = l·alpha + Σp and, if a row of
 // the wave moved its maximum, O·alpha.  Issued as wide independent passes.
-template <class T, class TL, bool MASK, bool GUARD>
+template <class T, class TL, bool MASK, bool GUARD, bool STEADY = false>
 __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[TL::QB], bool& any,
                                              SAcc<TL>& sacc, PFrag<TL>& pfr,
                                              const float (&mprev)[TL::QB],
@@ -625,7 +628,8 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
     row_sums(e, ls);
     bool need = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) need = need || (mprev[qb] == -__builtin_inff()) || !(ls[qb] <= psum_max);
+    for (int qb = 0; qb < QB; ++qb)
+      need = need || (!STEADY && mprev[qb] == -__builtin_inff()) || !(ls[qb] <= psum_max);
     slow = __builtin_amdgcn_ballot_w64(need) != 0;
   }
   if (slow) {
@@ -949,7 +953,7 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
       lds_t* const vbase = ring.base + NS * TL::K_TILE;
       lds_t* const k_i = R >= 0 ? ring.base + R * TL::K_TILE : ring.k(i);
       lds_t* const v_im1 = R >= 0 ? vbase + ((R + NS - 1) % NS) * TL::V_TILE : ring.v(i - 1);
-      mma_phase<T, TL, true, true>(ws, k_i, v_im1, sacc, pfr, mprev, mu, c, lane);
+      mma_phase<T, TL, true, true, true>(ws, k_i, v_im1, sacc, pfr, mprev, mu, c, lane);
       if (!lead) wait_vmem();
       __syncthreads();
       if (DEEP && lead) wait_vmem();
@@ -958,7 +962,8 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
       lds_t* const v_jm1 = R >= 0 ? vbase + ((R + 1) % NS) * TL::V_TILE : ring.v(j - 1);
       cp.k.issue(kh + (long long)(j * BN) * kss, k_j, qw);
       cp.v.issue(vh + (long long)((j - 1) * BN) * vss, v_jm1, qw);
-      ATTN_VPHASE(i, false);
+      softmax_tail<T, TL, false, CAUSAL, true>(ws, alpha, any, sacc, pfr, mprev, mu, i * BN, klg, thr,
+                                               psum_max, lane);
       if (!DEEP && lead) wait_vmem();
       __syncthreads();
     };
