@@ -186,8 +186,8 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const lds
 // HBM -> LDS copy of one K or V tile (rows kb .. kb+BN-1 of one head) into a
 // padded LDS tile of row stride STRIDE.  Each of the GW waves that share the
 // stream owns BPW of the tile's 1 KiB blocks (`wave` is the index among them); lane i of a block fills 16-byte slot i.  With LANE_ORDER, LDS
-// row p of each 32-row block receives key lane_key(p).  Pad slots are not
-// loaded.  The per-lane byte offsets do not depend on the tile, so they are
+// row p of each 32-row block receives key lane_key(p).  Pad slots receive
+// a copy of their row's first chunk (never read).  The per-lane byte offsets do not depend on the tile, so they are
 // computed once per kernel and a full tile costs one address add per block.
 template <class TL, int STRIDE, bool LANE_ORDER, int ROT = 0>
 struct DmaPlan {
@@ -957,7 +957,7 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
       if (!lead) wait_vmem();
       __syncthreads();
       if (DEEP && lead) wait_vmem();
-      const int j = i + ahead;
+      const int j = i + ahead;  // compile-time slots only occur with ahead == 2 (DEEP)
       lds_t* const k_j = R >= 0 ? ring.base + ((R + 2) % NS) * TL::K_TILE : ring.k(j);
       lds_t* const v_jm1 = R >= 0 ? vbase + ((R + 1) % NS) * TL::V_TILE : ring.v(j - 1);
       cp.k.issue(kh + (long long)(j * BN) * kss, k_j, qw);
