@@ -183,6 +183,24 @@ def test_ragged_lengths_all_variants(D, dtype):
             check_full(o, lse, q, k, v, scale, tag=f"S{S}/D{D}/{dtype}/v{var}")
 
 
+# Lengths whose steady loops (tiles minus four, per wave group) run zero to
+# sixteen steps, so the loop unrolled by the ring depth ends with every
+# remainder, with and without a ragged last tile.
+STEADY_LENGTHS = [320, 383, 448, 511, 576, 640, 700, 768, 900, 1024, 1280]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_steady_loop_lengths_all_variants(D, dtype):
+    for S in STEADY_LENGTHS:
+        q, k, v = W.gaussian_qkv(1, 2, S, D, dtype, seed=2000 + S)
+        scale = 1.0 / math.sqrt(D)
+        for var in variants_for(D, dtype):
+            say(f"steady S={S} D={D} {dtype} variant {var}")
+            o, lse = gpu_run(q, k, v, scale, variant=var)
+            check_full(o, lse, q, k, v, scale, tag=f"S{S}/D{D}/{dtype}/v{var}")
+
+
 def test_empty_problem_launches_nothing():
     q = torch.zeros(0, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
     o, lse = da.attn_fwd(q, q, q)
