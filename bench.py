@@ -145,8 +145,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the attention forward runs on one "
-              "device's share; no multi-GPU path). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: measures one GPU only (the attention forward runs on one device's "
+              "share; there is no multi-GPU path). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
