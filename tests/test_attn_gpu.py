@@ -326,22 +326,29 @@ def test_long_sequence_sampled():
     assert np.abs(lse[0, 0].cpu()[rows].double().numpy() - rl).max() <= LSE_MAX
 
 
-def test_tensors_past_4gib_sampled():
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+def test_tensors_past_4gib_sampled(layout):
     """Largest-size case: Q, K, V and O of 4.3 GB each, i.e. more than 2^31 elements,
-    so head offsets, K/V tile addresses and O/LSE stores of the last heads need more
-    than 32 bits.  Inputs are drawn on the device from a seeded generator (host
-    memory would not hold the float32 draws); sampled rows of the first head, the
-    heads on either side of element 2^31 and the last head are checked against
-    the oracle, which receives exactly the same rounded values."""
+    so head offsets, row offsets (BSHD), K/V tile addresses and O/LSE stores of the
+    last heads need more than 32 bits.  Inputs are drawn on the device from a seeded
+    generator (host memory would not hold the float32 draws); sampled rows of the
+    first head, the heads on either side of element 2^31 and the last head are
+    checked against the oracle, which receives exactly the same rounded values."""
     B, H, S, D = 2, 2056, 4096, 128
     assert B * H * S * D > 2**31
     scale = 1 / math.sqrt(D)
     g = torch.Generator(device="cuda")
     g.manual_seed(41)
-    q, k, v = (torch.randn((B, H, S, D), device="cuda", dtype=torch.bfloat16, generator=g)
+    shape = (B, H, S, D) if layout == "bhsd" else (B, S, H, D)
+    q, k, v = (torch.randn(shape, device="cuda", dtype=torch.bfloat16, generator=g)
                for _ in range(3))
-    say(f"  B={B} H={H} S={S} D={D}: {q.numel() * 2 / 2**30:.2f} GiB per tensor")
-    o, lse = da.attn_fwd_ex(q, k, v, scale=scale)
+    say(f"  {layout} B={B} H={H} S={S} D={D}: {q.numel() * 2 / 2**30:.2f} GiB per tensor")
+    if layout == "bhsd":
+        o, lse = da.attn_fwd_ex(q, k, v, scale=scale)
+    else:
+        q, k, v = (t.transpose(1, 2) for t in (q, k, v))
+        o = torch.empty(shape, device="cuda", dtype=torch.bfloat16).transpose(1, 2)
+        o, lse = da.attn_fwd_strided(q, k, v, o, scale=scale)
     torch.cuda.synchronize()
     rng = np.random.default_rng(41)
     heads_per_2g = 2**31 // (S * D)  # head index whose first element is element 2^31
@@ -352,7 +359,7 @@ def test_tensors_past_4gib_sampled():
         ro, rl = attention_rows(qs, ks, vs, scale, 0, 0, rows)
         e = np.abs(o[b, h].cpu()[rows].double().numpy() - ro)
         le = np.abs(lse[b, h].cpu()[rows].double().numpy() - rl).max()
-        say(f"  head {bh} (element offset {bh * S * D}): O max {e.max():.3e} LSE max {le:.3e}")
+        say(f"  b={b} h={h}: O max {e.max():.3e} LSE max {le:.3e}")
         assert e.max() <= O_MAX and e.mean() <= O_MEAN and le <= LSE_MAX, bh
     del q, k, v, o, lse
     torch.cuda.empty_cache()
