@@ -185,10 +185,12 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const lds
 
 // HBM -> LDS copy of one K or V tile (rows kb .. kb+BN-1 of one head) into a
 // padded LDS tile of row stride STRIDE.  Each of the GW waves that share the
-// stream owns BPW of the tile's 1 KiB blocks (`wave` is the index among them); lane i of a block fills 16-byte slot i.  With LANE_ORDER, LDS
-// row p of each 32-row block receives key lane_key(p).  Pad slots receive
-// a copy of their row's first chunk (never read).  The per-lane byte offsets do not depend on the tile, so they are
-// computed once per kernel and a full tile costs one address add per block.
+// stream (`wave` is the index among them) owns BPW of the tile's 1 KiB
+// blocks; lane i of a block fills 16-byte slot i.  With LANE_ORDER, LDS row p
+// of each 32-row block receives key lane_key(p).  Pad slots receive a copy of
+// their row's first chunk (never read).  The per-lane byte offsets do not
+// depend on the tile, so they are computed once per kernel and a full tile
+// costs one address add per block.
 template <class TL, int STRIDE, bool LANE_ORDER, int ROT = 0>
 struct DmaPlan {
   static constexpr int SPR = STRIDE / 16;              // 16-byte slots per LDS row
