@@ -580,9 +580,10 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
 // tile's row maximum exceeds it by more than thr.  Instead of taking every
 // tile's maximum, p = 2^x is computed against the kept m first: a lane whose
 // partial row sum is at most 2^thr has every p <= 2^thr, so none of its scores
-// exceeds m + thr and its row keeps m.  Only when some lane of the wave fails
-// that test (or m is still -inf, or the tile has masked keys) does the wave
-// take the maxima: each row's maximum over its visible keys, max(x) + mu,
+// exceeds m + thr and its row keeps m.  Masked keys get x = -inf first, so
+// their p is 0 and the same test holds on masked tiles.  Only when some lane
+// of the wave fails that test (or m is still -inf) does the wave take the
+// maxima: each row's maximum over its visible keys, max(x) + mu,
 // against m, the threshold-guarded move, the shift to the new reference, and
 // p again.  Rows that keep m get the same p either way.  Then the row-sum
 // partials in fp32, P rounded and packed, l = l·alpha + Σp and, if a row of
@@ -595,7 +596,14 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
                                              float thr, float psum_max, int lane) {
   constexpr int QB = TL::QB, NV = TL::BN / 32 * 16;
   int lim = klim - (kb + 16 * (lane >> 5));
-  if (MASK) asm volatile("" : "+v"(lim));
+  if (MASK) {
+    asm volatile("" : "+v"(lim));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        if ((v / 16) * 32 + (v % 16) >= lim) sacc[qb][v / 16][v % 16] = -__builtin_inff();
+  }
   auto exp2_all = [&](float (&e)[QB][NV], const float (&sh)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -609,7 +617,9 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
   auto row_sums = [&](float (&e)[QB][NV], float (&ls)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (MASK) {
+      // v_exp_f32 gives exactly 0 for the masked keys' -inf; exp2_poly clamps
+      // its argument, so its masked p are cleared here.
+      if (MASK && TL::POLY > 0) {
 #pragma unroll
         for (int v = 0; v < NV; ++v)
           if ((v / 16) * 32 + (v % 16) >= lim) e[qb][v] = 0.f;
@@ -623,28 +633,20 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
   float e[QB][NV], ls[QB], sh[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) sh[qb] = 0.f;
-  bool slow = MASK;
-  if (!MASK) {
-    exp2_all(e, sh);
-    __builtin_amdgcn_sched_barrier(0);
-    row_sums(e, ls);
-    bool need = false;
+  exp2_all(e, sh);
+  __builtin_amdgcn_sched_barrier(0);
+  row_sums(e, ls);
+  bool need = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      need = need || (!STEADY && mprev[qb] == -__builtin_inff()) || !(ls[qb] <= psum_max);
-    slow = __builtin_amdgcn_ballot_w64(need) != 0;
-  }
-  if (slow) {
+  for (int qb = 0; qb < QB; ++qb)
+    need = need || (!STEADY && mprev[qb] == -__builtin_inff()) || !(ls[qb] <= psum_max);
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
     any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float m4[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        float x = sacc[qb][v / 16][v % 16];
-        if (MASK && (v / 16) * 32 + (v % 16) >= lim) x = -__builtin_inff();
-        m4[v & 3] = fmaxf(m4[v & 3], x);
-      }
+      for (int v = 0; v < NV; ++v) m4[v & 3] = fmaxf(m4[v & 3], sacc[qb][v / 16][v % 16]);
       const float tx = lane_pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
       const float mcand = tx + mu[qb];  // tile row maximum over visible keys, log2 units
       const float mold = mprev[qb];
