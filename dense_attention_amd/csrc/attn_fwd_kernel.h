@@ -150,11 +150,13 @@ struct Tile {
   static constexpr int XCH = QB * (D / 32) * 4 + 1;
   // Waves per SIMD the register allocation targets.
   static constexpr int WPE = NW / 4;
-  // Shared K/V stream at D = 128: the MFMA phase runs at raised wave priority
-  // and the copy blocks of a tile are dealt to the waves round-robin (K blocks
-  // first, V blocks continuing where K left off), so every wave issues four
-  // or five.  Measured about 1% faster there, and slower on the key split.
-  static constexpr bool PRIO = !KSPLIT && D == 128;
+  // The MFMA phase runs at raised wave priority and the copy blocks of a tile
+  // are dealt to the waves round-robin (K blocks first, V blocks continuing
+  // where K left off), so every wave issues about as many.  Measured about 1%
+  // faster on the shared stream at D = 128, 1-2% on its key split and on the
+  // shared stream at D = 64; the key split at D = 64 keeps contiguous blocks
+  // (within noise there, and its registers would spill).
+  static constexpr bool PRIO = !(KSPLIT && D == 64);
   // D = 64: the Sᵀ and P·V MFMAs of a phase alternate (measured faster there;
   // at D = 128 the split softmax between the P·V MFMAs wins).
   static constexpr bool ALT = D == 64;
