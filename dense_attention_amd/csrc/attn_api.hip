@@ -22,6 +22,7 @@ using attn::Params;
 using attn::Tile;
 
 constexpr float kDefaultThreshold = 8.0f;  // log2 units
+constexpr float kMaxThresholdF16 = 15.0f;  // p <= 2^15 = 32768 is finite in fp16
 constexpr float kLog2e = 1.4426950408889634f;
 
 thread_local char g_last_error[256] = "";
@@ -196,6 +197,11 @@ int plan_launch(int B, int H, int Sq, int Skv, int D, int dtype, float scale,
     if (opts->grid < 0) return fail(ATTN_ERR_ARG, "grid must be >= 0");
     if (!(opts->rescale_threshold <= 64.0f) && !(opts->rescale_threshold < 0.0f))
       return fail(ATTN_ERR_ARG, "rescale_threshold must be <= 64");
+    // A kept maximum lets p reach 2^threshold, and P is rounded to the input
+    // type for P·V: fp16's largest finite value is 65504 < 2^16, so an fp16 P
+    // stays finite only up to threshold 15 (bf16 has fp32's exponent range).
+    if (dtype == ATTN_F16 && opts->rescale_threshold > kMaxThresholdF16)
+      return fail(ATTN_ERR_ARG, "rescale_threshold must be <= 15 for fp16 (P would overflow fp16)");
     if (opts->causal < 0 || opts->causal > 2) return fail(ATTN_ERR_ARG, "causal must be 0, 1 or 2");
   }
   // Rows are indexed with 32-bit integers inside a head and work items with
@@ -395,6 +401,41 @@ int forward(const Forward& f, const attn_fwd_options_t* opts, hipStream_t stream
   return launch_forward(f, plan, stream);
 }
 
+// attn_fwd_split: the partials of the key ranges go to the caller's workspace.
+int split_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int S, int D, float scale, int dtype, hipStream_t hs, int kv_splits,
+                  void* workspace, size_t workspace_bytes, const attn_fwd_options_t* opts) {
+  Plan plan;
+  int st = plan_launch(B, H, S, S, D, dtype, scale, opts, kv_splits == 0 ? 1 : kv_splits,
+                       /*need_device=*/false, &plan);
+  if (st != ATTN_OK) return st;
+  if (plan.empty) return ATTN_OK;
+  Forward f;
+  f.q = q; f.k = k; f.v = v; f.o = o; f.lse = lse;
+  f.B = B; f.H = H; f.Sq = S; f.Skv = S; f.D = D; f.scale = scale; f.dtype = dtype;
+  f.ql = f.kl = f.vl = f.ol = contiguous(H, S, D);
+  if ((st = check_pointers(f)) != ATTN_OK) return st;
+  st = plan_launch(B, H, S, S, D, dtype, scale, opts, kv_splits, /*need_device=*/true, &plan);
+  if (st != ATTN_OK) return st;
+  if (plan.n_splits == 1) return launch_forward(f, plan, hs);
+  const size_t need = split_ws_bytes(B, H, S, D, plan.n_splits);
+  if (!workspace) return fail(ATTN_ERR_NULL, "workspace must be non-null");
+  if (misaligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_ARG, "workspace is smaller than attn_fwd_split_workspace_size()");
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_o_bytes(B, H, S, D, plan.n_splits));
+  Forward part = f;
+  part.o = o_parts;
+  part.lse = lse_parts;
+  part.ol = contiguous(H, S, D);
+  part.o_f32 = true;
+  part.o_split = (long long)B * H * S * D;
+  part.lse_split = (long long)B * H * S;
+  if ((st = launch_forward(part, plan, hs)) != ATTN_OK) return st;
+  return launch_merge(o_parts, lse_parts, plan.n_splits, o, f.ol, lse, B, H, S, D, dtype, hs);
+}
+
 }  // namespace
 
 extern "C" {
@@ -493,35 +534,8 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
                    int S, int D, float scale, int dtype, void* stream, int kv_splits,
                    void* workspace, size_t workspace_bytes, const attn_fwd_options_t* opts) {
   g_last_error[0] = '\0';
-  Plan plan;
-  int st = plan_launch(B, H, S, S, D, dtype, scale, opts, kv_splits == 0 ? 1 : kv_splits,
-                       /*need_device=*/false, &plan);
-  if (st != ATTN_OK) return st;
-  if (plan.empty) return ATTN_OK;
-  Forward f;
-  f.q = q; f.k = k; f.v = v; f.o = o; f.lse = lse;
-  f.B = B; f.H = H; f.Sq = S; f.Skv = S; f.D = D; f.scale = scale; f.dtype = dtype;
-  f.ql = f.kl = f.vl = f.ol = contiguous(H, S, D);
-  if ((st = check_pointers(f)) != ATTN_OK) return st;
-  st = plan_launch(B, H, S, S, D, dtype, scale, opts, kv_splits, /*need_device=*/true, &plan);
-  if (st != ATTN_OK) return st;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (plan.n_splits == 1) return launch_forward(f, plan, hs);
-  const size_t need = split_ws_bytes(B, H, S, D, plan.n_splits);
-  if (!workspace) return fail(ATTN_ERR_NULL, "workspace must be non-null");
-  if (misaligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if (workspace_bytes < need) return fail(ATTN_ERR_ARG, "workspace is smaller than attn_fwd_split_workspace_size()");
-  float* o_parts = static_cast<float*>(workspace);
-  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_o_bytes(B, H, S, D, plan.n_splits));
-  Forward part = f;
-  part.o = o_parts;
-  part.lse = lse_parts;
-  part.ol = contiguous(H, S, D);
-  part.o_f32 = true;
-  part.o_split = (long long)B * H * S * D;
-  part.lse_split = (long long)B * H * S;
-  if ((st = launch_forward(part, plan, hs)) != ATTN_OK) return st;
-  return launch_merge(o_parts, lse_parts, plan.n_splits, o, f.ol, lse, B, H, S, D, dtype, hs);
+  return split_forward(q, k, v, o, lse, B, H, S, D, scale, dtype, static_cast<hipStream_t>(stream),
+                       kv_splits, workspace, workspace_bytes, opts);
 }
 
 int attn_get_config(int B, int H, int S, int D, int dtype, const attn_fwd_options_t* opts,

@@ -90,9 +90,14 @@ typedef struct attn_fwd_options {
    * only when a tile's maximum exceeds it by more than this, otherwise the
    * exponent absorbs the difference (P <= 2^threshold).  0 rescales whenever
    * the maximum grows (the textbook update).  Negative selects the default, 8.
-   * Must be <= 64.  ("B200 Attention Kernel from Scratch to Near-SOTA in 60
-   * Diagrams", Chapter 11 - Skip O rescale; "Attention for sm90, Line by Line",
-   * "What is rescale_threshold and when does it help?") */
+   * Must be <= 64 for ATTN_BF16 and <= 15 for ATTN_F16, else ATTN_ERR_ARG: P
+   * is rounded to the input type before P·V, and a kept maximum lets p reach
+   * 2^threshold, which must stay finite in that type (fp16 ends at 65504 <
+   * 2^16; bf16 and the fp32 sums hold 2^64 times any row's length).  ("B200
+   * Attention Kernel from Scratch to Near-SOTA in 60 Diagrams", Chapter 11 -
+   * Skip O rescale: skipping is allowed while no intermediate value
+   * overflows; "Attention for sm90, Line by Line", "What is rescale_threshold
+   * and when does it help?") */
   float rescale_threshold;
   /* Kernel tile variant, 0 = the library's choice; otherwise an id listed by
    * attn_variant_info().  A variant must support D and dtype. */

@@ -106,6 +106,21 @@ def test_rejects_bad_options(lib):
     o = da.attn_fwd_options()
     o.variant = 12345
     assert _call(lib, opts=o) == -8
+    # fp16 P holds at most 65504 < 2^16: thresholds above 15 are refused for
+    # fp16 only (bf16 keeps the bound of 64).
+    for thr, dtype, want in [(15.0, 0, "ok"), (15.5, 0, -8), (16.0, 0, -8), (64.0, 0, -8),
+                             (16.0, 1, "ok"), (64.0, 1, "ok")]:
+        o = da.attn_fwd_options()
+        o.rescale_threshold = thr
+        if want == "ok":
+            # attn_get_config validates exactly as attn_fwd_ex and never launches:
+            # 0 on a gfx950 device, ATTN_ERR_DEVICE without one, never ATTN_ERR_ARG
+            cfg = da.attn_config()
+            st = lib.attn_get_config(1, 1, 16, 64, dtype, ctypes.byref(o), ctypes.byref(cfg))
+            assert st in (0, -6), (thr, dtype, st)
+        else:
+            assert _call(lib, dtype=dtype, opts=o) == want, (thr, dtype)
+            assert "15" in lib.attn_last_error().decode()
     o = da.attn_fwd_options()
     o.grid = -3
     assert _call(lib, opts=o) == -8
@@ -264,3 +279,4 @@ def test_library_shares_torch_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+

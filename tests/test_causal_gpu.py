@@ -15,7 +15,8 @@ import torch
 
 import dense_attention_amd as da
 import workloads as W
-from oracle import attention_forward, attention_rows
+from oracle import attention_forward
+from tests.oracle_by_head import forward_by_head
 
 pytestmark = pytest.mark.gpu
 
@@ -84,25 +85,15 @@ def test_causal_s4096_d64_fp16_full():
 
 
 @pytest.mark.parametrize("name", ["b4_h16_s4096_d128_bf16", "b2_h16_s8192_d128_bf16"])
-def test_causal_hd128_sampled(name):
+def test_causal_hd128_full(name):
+    """The hd128 workloads with the causal mask, every element against the oracle."""
     w = W.BY_NAME[name]
     q, k, v = W.workload_qkv(w)
     say(f"{w.name} causal")
     o, lse = da.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
     torch.cuda.synchronize()
-    go, gl = o.cpu(), lse.cpu().double().numpy()
-    qn, kn, vn = W.to_f64(q), W.to_f64(k), W.to_f64(v)
-    rng = np.random.default_rng(3000)
-    errs, worst_l = [], 0.0
-    for (b, h) in [(0, 0), (w.B - 1, w.H - 1), (0, w.H // 2)]:
-        rows = np.unique(np.concatenate([rng.choice(w.S, 40, replace=False),
-                                         [0, 1, 63, 64, 255, 256, w.S // 2, w.S - 256, w.S - 1]]))
-        ro, rl = attention_rows(qn, kn, vn, w.scale, b, h, rows, causal_offset=0)
-        errs.append(np.abs(go[b, h, rows].double().numpy() - ro))
-        worst_l = max(worst_l, np.abs(gl[b, h, rows] - rl).max())
-    e = np.concatenate([x.ravel() for x in errs])
-    say(f"  sampled O max {e.max():.3e} mean {e.mean():.3e} LSE max {worst_l:.3e}")
-    assert e.max() <= O_MAX and e.mean() <= O_MEAN and worst_l <= LSE_MAX
+    ro, rl = forward_by_head(q, k, v, w.scale, causal_offset=0)
+    compare(o, lse, ro, rl, f"{w.name} causal, whole output")
 
 
 @pytest.mark.parametrize("Sq,Skv,offset", [(100, 300, None), (300, 100, None), (257, 257, 64),
@@ -175,6 +166,10 @@ def test_causal_grid_sizes_agree():
     q, k, v = W.gaussian_qkv(2, 4, 1111, 128, "bf16", seed=3500)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     ref, ref_l = da.attn_fwd_ex(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / math.sqrt(128),
+                               causal_offset=0)
+    compare(ref, ref_l, ro, rl, "causal grid reference launch")
     for g in [1, 7, 64]:
         o, lse = da.attn_fwd_ex(qd, kd, vd, causal=True, grid=g)
         torch.cuda.synchronize()

@@ -147,8 +147,11 @@ def test_with_kv_ranges_and_strided_layouts(D, dtype):
 def test_grid_sizes_agree_bit_for_bit():
     q, k, v = W.gaussian_qkv(1, 3, 777, 64, "fp16", seed=4300)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), 1 / math.sqrt(64))
     for var in split_variants(64, "fp16"):
         ref, ref_l = da.attn_fwd_ex(qd, kd, vd, variant=var)
+        torch.cuda.synchronize()
+        compare(ref, ref_l, ro, rl, f"grid reference launch v{var}")
         for g in [1, 5, 8, 17]:
             o, lse = da.attn_fwd_ex(qd, kd, vd, variant=var, grid=g)
             torch.cuda.synchronize()

@@ -29,6 +29,58 @@ def test_rows_api_matches_full_forward():
     np.testing.assert_allclose(l_r, lse[1, 2, rows], rtol=0, atol=1e-13)
 
 
+def _rows_match_full_forward(rows_fn):
+    """attention_rows with a causal mask against the matching rows of the pinned full
+    forward: offsets 0, -7 and 13, queries fewer and more than keys, scattered
+    rows that include rows without any visible key (O = 0, LSE = -inf)."""
+    rng = np.random.default_rng(5)
+    for Sq, Skv in [(40, 40), (40, 57), (57, 23)]:
+        q = rng.standard_normal((2, 2, Sq, 8))
+        k, v = (rng.standard_normal((2, 2, Skv, 8)) for _ in range(2))
+        for off in (0, -7, 13):
+            o, lse = attention_forward(q, k, v, 0.3, row_block=16, causal_offset=off)
+            rows = [Sq - 1, 0, 3, 6, 7, 11, 20, Sq // 2, Sq - 2]
+            for (b, h) in [(0, 1), (1, 0)]:
+                o_r, l_r = rows_fn(q, k, v, 0.3, b, h, rows, causal_offset=off)
+                np.testing.assert_allclose(o_r, o[b, h, rows], rtol=0, atol=1e-13)
+                np.testing.assert_array_equal(np.isneginf(l_r), np.isneginf(lse[b, h, rows]))
+                fin = np.isfinite(lse[b, h, rows])
+                np.testing.assert_allclose(l_r[fin], lse[b, h, rows][fin], rtol=0, atol=1e-13)
+            if off == -7:   # rows 0..6 see no key: the keyless branch is exercised
+                assert np.isneginf(lse[:, :, :7]).all() and not np.isneginf(lse[:, :, 7:]).any()
+
+
+def test_rows_api_causal_matches_full_forward():
+    _rows_match_full_forward(attention_rows)
+
+
+def _r_row_positions(q, k, v, scale, b, h, rows, causal_offset=None):
+    # slip: the mask built for positions 0..len(rows)-1 instead of the rows asked for
+    rows = np.asarray(rows, dtype=np.int64)
+    qh = np.asarray(q[b, h], dtype=np.float64)[rows]
+    kh, vh = np.asarray(k[b, h], dtype=np.float64), np.asarray(v[b, h], dtype=np.float64)
+    mask = None if causal_offset is None else oa.causal_mask(range(len(rows)), kh.shape[0],
+                                                             causal_offset)
+    return oa._rows(qh, kh, vh, scale, mask)
+
+
+def _r_offset_ignored(q, k, v, scale, b, h, rows, causal_offset=None):
+    # slip: the offset dropped (mask j <= i)
+    return attention_rows(q, k, v, scale, b, h, rows, None if causal_offset is None else 0)
+
+
+def _r_wrong_head(q, k, v, scale, b, h, rows, causal_offset=None):
+    # slip: keys and values of the head with the indices swapped
+    return attention_rows(q, k, v, scale, h, b, rows, causal_offset)
+
+
+@pytest.mark.parametrize("mutant", [_r_row_positions, _r_offset_ignored, _r_wrong_head],
+                         ids=lambda f: f.__name__)
+def test_planted_rows_mistake_fails_rows_pin(mutant):
+    with pytest.raises(AssertionError):
+        _rows_match_full_forward(mutant)
+
+
 def test_row_blocking_does_not_change_result():
     rng = np.random.default_rng(4)
     q, k, v = (rng.standard_normal((1, 2, 130, 8)) for _ in range(3))
