@@ -16,7 +16,8 @@ import threading
 __all__ = [
     "ATTN_F16", "ATTN_BF16", "ATTN_F32", "AttnError", "attn_fwd", "attn_fwd_ex",
     "attn_fwd_strided", "attn_fwd_partial", "attn_merge", "attn_fwd_split",
-    "attn_fwd_split_workspace_size", "attn_get_config", "attn_variants", "attn_strerror",
+    "attn_fwd_split_workspace_size", "attn_fwd_split_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "attn_get_config", "attn_variants", "attn_strerror",
     "library_path", "load_library",
 ]
 
@@ -27,8 +28,11 @@ ATTN_F32 = 2
 STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_DTYPE", -3: "ATTN_ERR_SHAPE",
     -4: "ATTN_ERR_ALIGN", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_DEVICE", -7: "ATTN_ERR_LAUNCH",
-    -8: "ATTN_ERR_ARG",
+    -8: "ATTN_ERR_ARG", -9: "ATTN_ERR_SCRATCH",
 }
+
+# Size of the static device scratch behind attn_fwd_split_noalloc (attn.h).
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -110,6 +114,8 @@ def load_library(path: str | None = None):
         lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp,
                                        ctypes.c_size_t, op]
         lib.attn_fwd_split.restype = i
+        lib.attn_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, op]
+        lib.attn_fwd_split_noalloc.restype = i
         lib.attn_strerror.argtypes = [i]
         lib.attn_strerror.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
@@ -396,5 +402,38 @@ def attn_fwd_split(q, k, v, o=None, lse=None, scale=None, *, kv_splits=0, worksp
                                 float(scale), _dtype_code(q), stream.cuda_stream, int(kv_splits),
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 ctypes.byref(opts))
+    _check(lib, st)
+    return o, lse
+
+
+def attn_fwd_split_noalloc(q, k, v, o, lse=None, scale=None, *, kv_splits=0, stream=None,
+                           rescale_threshold=None, variant=0, grid=0, causal=False):
+    """attn_fwd_split whose key-range partials live in the library's static device
+    scratch (NOALLOC_SCRATCH_BYTES per device): the library call allocates
+    nothing.  ``o`` (and ``lse``, if wanted) must be given, so that this
+    wrapper allocates nothing either.  Calls that may overlap on one device
+    share the scratch and must be ordered by the caller."""
+    import torch
+
+    lib = load_library()
+    B, H, S, Skv, D = _check_inputs(q, k, v)
+    if Skv != S or not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, S, D] tensors of one shape")
+    if o is None or o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() \
+            or o.device != q.device:
+        raise ValueError("o must be given: a contiguous tensor like q")
+    if lse is not None and (tuple(lse.shape) != (B, H, S) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    opts = _options(rescale_threshold, variant, grid, causal)
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_split_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr() if lse is not None else None, B, H, S, D,
+                                        float(scale), _dtype_code(q), stream.cuda_stream,
+                                        int(kv_splits), ctypes.byref(opts))
     _check(lib, st)
     return o, lse

@@ -14,6 +14,17 @@
 #include "attn_fwd_kernel.h"
 #include "attn_merge_kernel.h"
 
+// Static scratch of attn_fwd_split_noalloc: the fp32 partials of the key
+// ranges live here instead of in a caller workspace.  In host code `scratch`
+// only names the symbol (a host-side stand-in, not a device address); the
+// device address, one per device, comes from hipGetSymbolAddress on the entry
+// point's first call on that device and is the only form host code passes on.
+// Every call on a device shares that device's copy, so calls that overlap on
+// one device race.  Nothing in it needs to start at zero: the partial kernel
+// writes every element the merge reads.
+static_assert(ATTN_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using attn::BF16;
@@ -401,15 +412,59 @@ int forward(const Forward& f, const attn_fwd_options_t* opts, hipStream_t stream
   return launch_forward(f, plan, stream);
 }
 
-// attn_fwd_split: the partials of the key ranges go to the caller's workspace.
+struct ScratchSlot {
+  void* ptr = nullptr;
+  hipError_t err = hipErrorNotInitialized;
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of this device's scratch (the current device must be the one
+// the call runs on).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_DEVICE, "no current HIP device");
+  std::call_once(g_scratch_once[dev], [dev]() {
+    ScratchSlot& sl = g_scratch[dev];
+    void* ptr = nullptr;
+    sl.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    sl.ptr = sl.err == hipSuccess ? ptr : nullptr;
+  });
+  const ScratchSlot& sl = g_scratch[dev];
+  if (sl.err != hipSuccess || sl.ptr == nullptr) {
+    char buf[200];
+    std::snprintf(buf, sizeof(buf), "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(sl.err));
+    return fail(ATTN_ERR_LAUNCH, buf);
+  }
+  *out = sl.ptr;
+  return ATTN_OK;
+}
+
+int scratch_too_small(size_t need) {
+  char buf[200];
+  std::snprintf(buf, sizeof(buf),
+                "the key-range partials need %zu bytes; the static scratch holds %zu "
+                "(use fewer kv_splits, or attn_fwd_split with a workspace)",
+                need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+  return fail(ATTN_ERR_SCRATCH, buf);
+}
+
+// attn_fwd_split and attn_fwd_split_noalloc: the partials of the key ranges
+// go to the caller's workspace, or to the static scratch.
 int split_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int S, int D, float scale, int dtype, hipStream_t hs, int kv_splits,
-                  void* workspace, size_t workspace_bytes, const attn_fwd_options_t* opts) {
+                  void* workspace, size_t workspace_bytes, bool static_scratch,
+                  const attn_fwd_options_t* opts) {
   Plan plan;
   int st = plan_launch(B, H, S, S, D, dtype, scale, opts, kv_splits == 0 ? 1 : kv_splits,
                        /*need_device=*/false, &plan);
   if (st != ATTN_OK) return st;
   if (plan.empty) return ATTN_OK;
+  // An explicit range count fixes the scratch size before any device query.
+  if (static_scratch && kv_splits > 0 && plan.n_splits > 1 &&
+      split_ws_bytes(B, H, S, D, plan.n_splits) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+    return scratch_too_small(split_ws_bytes(B, H, S, D, plan.n_splits));
   Forward f;
   f.q = q; f.k = k; f.v = v; f.o = o; f.lse = lse;
   f.B = B; f.H = H; f.Sq = S; f.Skv = S; f.D = D; f.scale = scale; f.dtype = dtype;
@@ -419,10 +474,16 @@ int split_forward(const void* q, const void* k, const void* v, void* o, float* l
   if (st != ATTN_OK) return st;
   if (plan.n_splits == 1) return launch_forward(f, plan, hs);
   const size_t need = split_ws_bytes(B, H, S, D, plan.n_splits);
-  if (!workspace) return fail(ATTN_ERR_NULL, "workspace must be non-null");
-  if (misaligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(ATTN_ERR_ARG, "workspace is smaller than attn_fwd_split_workspace_size()");
+  if (static_scratch) {
+    if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return scratch_too_small(need);
+    if ((st = scratch_address(&workspace)) != ATTN_OK) return st;
+    workspace_bytes = ATTN_NOALLOC_SCRATCH_BYTES;
+  } else {
+    if (!workspace) return fail(ATTN_ERR_NULL, "workspace must be non-null");
+    if (misaligned(workspace, 256)) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(ATTN_ERR_ARG, "workspace is smaller than attn_fwd_split_workspace_size()");
+  }
   float* o_parts = static_cast<float*>(workspace);
   float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_o_bytes(B, H, S, D, plan.n_splits));
   Forward part = f;
@@ -535,7 +596,15 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
                    void* workspace, size_t workspace_bytes, const attn_fwd_options_t* opts) {
   g_last_error[0] = '\0';
   return split_forward(q, k, v, o, lse, B, H, S, D, scale, dtype, static_cast<hipStream_t>(stream),
-                       kv_splits, workspace, workspace_bytes, opts);
+                       kv_splits, workspace, workspace_bytes, /*static_scratch=*/false, opts);
+}
+
+int attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int S, int D, float scale, int dtype, void* stream, int kv_splits,
+                           const attn_fwd_options_t* opts) {
+  g_last_error[0] = '\0';
+  return split_forward(q, k, v, o, lse, B, H, S, D, scale, dtype, static_cast<hipStream_t>(stream),
+                       kv_splits, nullptr, 0, /*static_scratch=*/true, opts);
 }
 
 int attn_get_config(int B, int H, int S, int D, int dtype, const attn_fwd_options_t* opts,
@@ -587,6 +656,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_DEVICE: return "no gfx950 device";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_ARG: return "invalid option";
+    case ATTN_ERR_SCRATCH: return "problem needs more than the static scratch";
     default: return "unknown status";
   }
 }

@@ -62,7 +62,8 @@ enum attn_status {
   ATTN_ERR_SCALE = -5,   /* scale is NaN or infinite */
   ATTN_ERR_DEVICE = -6,  /* no current HIP device, or it is not a gfx950 GPU */
   ATTN_ERR_LAUNCH = -7,  /* the kernel launch failed (attn_last_error() has the HIP text) */
-  ATTN_ERR_ARG = -8      /* an option is out of range */
+  ATTN_ERR_ARG = -8,     /* an option is out of range */
+  ATTN_ERR_SCRATCH = -9  /* attn_fwd_split_noalloc: the partials exceed the static scratch */
 };
 
 /*
@@ -258,6 +259,33 @@ size_t attn_fwd_split_workspace_size(int B, int H, int S, int D, int kv_splits);
 int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int S, int D, float scale, int dtype, void* stream, int kv_splits,
                    void* workspace, size_t workspace_bytes, const attn_fwd_options_t* opts);
+
+/*
+ * attn_fwd_split_noalloc — attn_fwd_split for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The fp32 partials of the
+ * key ranges go to a static device array of ATTN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every device it runs on until the process ends; the call
+ * itself allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine).
+ *
+ *   kv_splits  as attn_fwd_split.  A problem whose partials,
+ *              attn_fwd_split_workspace_size(B, H, S, D, n) bytes for the n
+ *              ranges used, exceed ATTN_NOALLOC_SCRATCH_BYTES is refused with
+ *              ATTN_ERR_SCRATCH and nothing is launched (with kv_splits > 0
+ *              before any device query).  With a single range no scratch is
+ *              used.
+ *
+ * Every call on one device shares that device's scratch: calls that may
+ * overlap on a device (different streams, threads) race and must be ordered
+ * by the caller, e.g. on one stream.  The scratch holds the last call's
+ * partials afterwards; nothing in it has to be cleared between calls.  Other
+ * arguments and errors as attn_fwd_split.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int S, int D, float scale, int dtype, void* stream,
+                           int kv_splits, const attn_fwd_options_t* opts);
 
 /* Static description of a status code.  Never NULL. */
 const char* attn_strerror(int status);

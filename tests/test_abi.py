@@ -156,7 +156,7 @@ def test_variant_table(lib):
 
 
 def test_strerror_covers_every_status(lib):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, 7]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 7]:
         s = lib.attn_strerror(code)
         assert s is not None and len(s) > 0
 
@@ -280,3 +280,25 @@ def test_library_shares_torch_hip_runtime():
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
 
+
+def test_noalloc_refuses_partials_beyond_the_static_scratch(lib):
+    """With an explicit range count the scratch size is known before any device
+    query: a problem whose partials exceed the static scratch is refused with
+    ATTN_ERR_SCRATCH and nothing is launched."""
+    f = ctypes.c_float(0.1)
+    B, H, S, D, n = 1, 16, 4096, 128, 8          # 8 ranges: 256 MiB of fp32 partials
+    need = lib.attn_fwd_split_workspace_size(B, H, S, D, n)
+    assert need > da.NOALLOC_SCRATCH_BYTES
+    st = lib.attn_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, None, B, H, S, D, f, da.ATTN_BF16,
+                                    None, n, None)
+    assert st == -9
+    assert str(need) in lib.attn_last_error().decode()
+    # same validation as attn_fwd_split before that
+    assert lib.attn_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 512, 64, f, da.ATTN_F16,
+                                      None, 65, None) == -8
+    assert lib.attn_fwd_split_noalloc(None, None, None, None, None, 0, 1, 512, 64, f, da.ATTN_F16,
+                                      None, 2, None) == 0
+    # the header's size is the binding's
+    text = open(HEADER).read()
+    assert "#define ATTN_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)" in text
+    assert da.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
