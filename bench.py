@@ -148,7 +148,9 @@ class ClockSampler:
 
     def sample_during(self, busy, ms: float):
         """Runs ``busy()`` repeatedly for about ``ms`` milliseconds while a thread
-        reads the clock every 5 ms; returns (median MHz, median W) or Nones."""
+        reads the clock every 20 ms; returns the median MHz and W of the readings
+        taken after the first second.  The firmware refreshes these metrics about
+        once a second, so earlier readings can still describe the load before."""
         import threading
         import torch
         if self.handle is None:
@@ -156,15 +158,17 @@ class ClockSampler:
         clks, pws, stop = [], [], threading.Event()
 
         def poll():
+            t_start = time.perf_counter()
             while not stop.is_set():
                 try:
                     c, p = self.read()
-                    clks.append(c)
-                    if p is not None:
-                        pws.append(p)
+                    if time.perf_counter() - t_start >= 1.0:
+                        clks.append(c)
+                        if p is not None:
+                            pws.append(p)
                 except Exception:
                     pass
-                time.sleep(0.005)
+                time.sleep(0.02)
 
         th = threading.Thread(target=poll, daemon=True)
         t0 = time.perf_counter()
@@ -301,9 +305,10 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed back-to-back launches before the warmup steps, so GPU clocks "
                          "reach their loaded steady state (0 disables)")
-    ap.add_argument("--clock-ms", type=float, default=200.0,
+    ap.add_argument("--clock-ms", type=float, default=1300.0,
                     help="untimed launches after each timed region while amd-smi samples the "
-                         "shader clock and power (0 disables)")
+                         "shader clock and power; readings count after the first second "
+                         "(0 disables)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(calibrates the HBM byte counters of rocprofv3)")

@@ -22,9 +22,10 @@
 // Memory path: K and V tiles go from HBM straight into LDS
 // (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at base + 16·i,
 // so the LDS placement of every 16-byte chunk is chosen through the global
-// address each lane loads).  LDS rows are padded (K: +16 bytes, V: +64 or +48)
-// so that every LDS read is a per-lane base plus an immediate offset and no
-// two lanes of a 64-bank pass hit the same bank:
+// address each lane loads).  LDS rows are padded (K: +16 bytes, V: +64) so
+// that every LDS read is a per-lane base plus an immediate offset and no two
+// lanes of a 64-bank pass hit the same bank; where padded V rows do not fit,
+// V rows are unpadded and swizzled instead (Tile::VSWZ):
 //   * K rows are stored in MFMA-lane order (LDS row p of a 32-row block holds
 //     key lane_key(p)); the A operand of Sᵀ is one ds_read_b128 per lane;
 //   * V rows are stored in key order; the A operand of Oᵀ comes from two
@@ -64,6 +65,10 @@ struct Mma<BF16> {
     bf16x2_t r = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, r);
   }
+  // Row sums come from the fp32 p: bf16's rounding (up to 2^-9 relative)
+  // would move the LSE of a short or one-key-dominated row by up to 2e-3.
+  static constexpr bool PACKED_SUMS = false;
+  static __device__ __forceinline__ float sum2(uint32_t, float acc) { return acc; }
 };
 
 template <>
@@ -75,6 +80,15 @@ struct Mma<F16> {
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     f16x2_t r = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, r);
+  }
+  // Row sums come from the rounded P itself, one v_dot2c_f32_f16 against
+  // (1, 1) per packed pair: half the additions of summing the fp32 p.  fp16
+  // rounds P to within 2^-11 relative, which moves a row's LSE by at most
+  // 4.9e-4, and O and its normaliser then see the same P.
+  static constexpr bool PACKED_SUMS = true;
+  static __device__ __forceinline__ float sum2(uint32_t pk, float acc) {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk), one, acc, false);
   }
 };
 
@@ -136,9 +150,12 @@ struct Tile {
   static constexpr int DC = D / 8;          // 16-byte chunks per row
   static constexpr int RINGS = KSPLIT ? 2 : 1;
   static constexpr int KS = D * 2 + 16;     // LDS row stride of K (bytes)
-  // LDS row stride of V (bytes): 64 bytes of padding, or 48 where two-deep
-  // rings would not fit in LDS otherwise.
-  static constexpr int VS = 2 * RINGS * BN * (KS + D * 2 + 64) <= 160 * 1024 ? D * 2 + 64 : D * 2 + 48;
+  // LDS rows of V: padded by 64 bytes, or, where two-deep rings of padded
+  // rows would not fit in LDS (the key split at D = 64 with 128-key tiles),
+  // unpadded with bit 2 of the 16-byte chunk index XOR-ed with bit 1 of the
+  // row (VSWZ), which keeps the transposed operand reads conflict-free.
+  static constexpr bool VSWZ = 2 * RINGS * BN * (KS + D * 2 + 64) > 160 * 1024;
+  static constexpr int VS = VSWZ ? D * 2 : D * 2 + 64;
   static constexpr int K_TILE = BN * KS;
   static constexpr int V_TILE = BN * VS;
   // K/V ring depth: three tiles when they fit in LDS, else two.
@@ -161,6 +178,7 @@ struct Tile {
   // at D = 128 the split softmax between the P·V MFMAs wins).
   static constexpr bool ALT = D == 64;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile sizes");
+  static_assert(!VSWZ || D == 64, "the V swizzle assumes 128-byte rows");
   static_assert(K_TILE % 1024 == 0 && V_TILE % 1024 == 0, "tiles must be whole DMA blocks");
   static_assert(!KSPLIT || NW == 8, "a key split pairs two groups of four waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -190,10 +208,11 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const lds
 // stream (`wave` is the index among them) owns BPW of the tile's 1 KiB
 // blocks; lane i of a block fills 16-byte slot i.  With LANE_ORDER, LDS row p
 // of each 32-row block receives key lane_key(p).  Pad slots receive a copy of
-// their row's first chunk (never read).  The per-lane byte offsets do not
+// their row's first chunk (never read).  With SWZ (unpadded rows), slot c of
+// row p receives chunk c ^ (4·bit 1 of p).  The per-lane byte offsets do not
 // depend on the tile, so they are computed once per kernel and a full tile
 // costs one address add per block.
-template <class TL, int STRIDE, bool LANE_ORDER, int ROT = 0>
+template <class TL, int STRIDE, bool LANE_ORDER, int ROT = 0, bool SWZ = false>
 struct DmaPlan {
   static constexpr int SPR = STRIDE / 16;              // 16-byte slots per LDS row
   static constexpr int BLOCKS = TL::BN * SPR / 64;     // 1 KiB blocks per tile
@@ -213,6 +232,7 @@ struct DmaPlan {
     const int p = slot / SPR;
     c = slot - p * SPR;
     if (c >= TL::DC) c = 0;
+    if (SWZ) c ^= ((p >> 1) & 1) << 2;
     key = LANE_ORDER ? ((p & ~31) | lane_key(p & 31)) : p;
   }
 
@@ -373,7 +393,7 @@ struct Ring {
 template <class TL>
 struct Copies {
   DmaPlan<TL, TL::KS, true> k;
-  DmaPlan<TL, TL::VS, false, (TL::BN * TL::KS / 1024) % TL::GW> v;
+  DmaPlan<TL, TL::VS, false, (TL::BN * TL::KS / 1024) % TL::GW, TL::VSWZ> v;
 };
 
 // Epilogue of a work item: O / l (rounded to the output type, or fp32 for a
@@ -476,13 +496,19 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
   const int g = lane >> 4;
   const int li = lane & 15;
   uint32_t ka = (uint32_t)(uintptr_t)kl + (uint32_t)((lane & 31) * TL::KS + (lane >> 5) * 16);
-  uint32_t va = (uint32_t)(uintptr_t)vl + (uint32_t)((16 * (g >> 1) + (li >> 2)) * TL::VS +
-                                                      (2 * (li & 1) + (g & 1)) * 16 +
-                                                      ((li >> 1) & 1) * 8);
+  const int vrow = 16 * (g >> 1) + (li >> 2);
+  int vchunk = 2 * (li & 1) + (g & 1);
+  if (TL::VSWZ) vchunk ^= ((vrow >> 1) & 1) << 2;
+  uint32_t va = (uint32_t)(uintptr_t)vl + (uint32_t)(vrow * TL::VS + vchunk * 16 + ((li >> 1) & 1) * 8);
+  // Swizzled V: the second 64 bytes of a row (db = 1) sit at the address with
+  // bit 6 flipped, which no immediate offset expresses; a second base.
+  uint32_t va1 = va ^ 64u;
   if (QK) asm volatile("" : "+v"(ka));
   if (PV) asm volatile("" : "+v"(va));
+  if (PV && TL::VSWZ) asm volatile("" : "+v"(va1));
   const lds_t* kbase = (const lds_t*)(uintptr_t)ka;
   const lds_t* vbase = (const lds_t*)(uintptr_t)va;
+  const lds_t* vbase1 = (const lds_t*)(uintptr_t)va1;
   // Operand of slot s: a K fragment for an Sᵀ MFMA (key block s % NB, head-dim
   // step s / NB) or a V fragment for a P·V MFMA: lane group g = lane/16
   // covers key half g/2 and head-dim half g%2; inside the group, lane i reads
@@ -501,7 +527,8 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
     }
     const int i = pv_index(s);
     const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
-    const lds_t* pv0 = vbase + (nb * 32 + 8 * mm) * TL::VS + db * 64;
+    const lds_t* pv0 = (TL::VSWZ ? (db == 0 ? vbase : vbase1) : vbase + db * 64) +
+                       (nb * 32 + 8 * mm) * TL::VS;
     const u32x2_t lo = ld_lds_tr(pv0);
     const u32x2_t hi = ld_lds_tr(pv0 + 4 * TL::VS);
     const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
@@ -580,16 +607,18 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
 // The lazy rescale (reading of "B200 Attention Kernel from Scratch to
 // Near-SOTA in 60 Diagrams", Chapter 11) moves the kept maximum m only when a
 // tile's row maximum exceeds it by more than thr.  Instead of taking every
-// tile's maximum, p = 2^x is computed against the kept m first: a lane whose
-// partial row sum is at most 2^thr has every p <= 2^thr, so none of its scores
-// exceeds m + thr and its row keeps m.  Masked keys get x = -inf first, so
-// their p is 0 and the same test holds on masked tiles.  Only when some lane
-// of the wave fails that test (or m is still -inf) does the wave take the
-// maxima: each row's maximum over its visible keys, max(x) + mu,
-// against m, the threshold-guarded move, the shift to the new reference, and
-// p again.  Rows that keep m get the same p either way.  Then the row-sum
-// partials in fp32, P rounded and packed, l = l·alpha + Σp and, if a row of
-// the wave moved its maximum, O·alpha.  Issued as wide independent passes.
+// tile's maximum, p = 2^x is computed against the kept m first, and its
+// lane-partial row sum in fp32 (for fp16, the sum of P rounded to fp16; see
+// Mma<F16>::sum2).  A lane whose partial row sum is at most 2^thr has every
+// p <= 2^thr, so none of its scores exceeds m + thr (up to P's rounding) and
+// its row keeps m.  Masked keys get x = -inf first, so their p is 0 and the
+// same test holds on masked tiles.  Only when some lane of the wave fails
+// that test (or m is still -inf) does the wave take the maxima: each row's
+// maximum over its visible keys, max(x) + mu, against m, the
+// threshold-guarded move, the shift to the new reference, and P and its sums
+// again.  Rows that keep m get the same P either way.  Then l = l·alpha + ΣP
+// and, if a row of the wave moved its maximum, O·alpha.  Issued as wide
+// independent passes.
 template <class T, class TL, bool MASK, bool GUARD, bool STEADY = false>
 __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[TL::QB], bool& any,
                                              SAcc<TL>& sacc, PFrag<TL>& pfr,
@@ -616,7 +645,10 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
                                                                              : __builtin_amdgcn_exp2f(x);
       }
   };
-  auto row_sums = [&](float (&e)[QB][NV], float (&ls)[QB]) {
+  // Lane-partial row sums.  fp16: P rounded and packed (the B operand of the
+  // next P·V) first, then the sums of exactly that P, one dot2 per packed
+  // pair.  bf16: the sums of the fp32 p; P is packed after the last pass.
+  auto pack_sums = [&](float (&e)[QB][NV], float (&ls)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // v_exp_f32 gives exactly 0 for the masked keys' -inf; exp2_poly clamps
@@ -626,24 +658,46 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
         for (int v = 0; v < NV; ++v)
           if ((v / 16) * 32 + (v % 16) >= lim) e[qb][v] = 0.f;
       }
-      float l4[4] = {e[qb][0], e[qb][1], e[qb][2], e[qb][3]};
+      float l4[4];
+      if (Mma<T>::PACKED_SUMS) {
 #pragma unroll
-      for (int v = 4; v < NV; ++v) l4[v & 3] += e[qb][v];
+        for (int w = 0; w < NV / 2; ++w)
+          pfr[qb][w / 8][w % 8] = Mma<T>::pack(e[qb][2 * w], e[qb][2 * w + 1]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) l4[w] = Mma<T>::sum2(pfr[qb][w / 8][w % 8], 0.f);
+#pragma unroll
+        for (int w = 4; w < NV / 2; ++w) l4[w & 3] = Mma<T>::sum2(pfr[qb][w / 8][w % 8], l4[w & 3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) l4[v] = e[qb][v];
+#pragma unroll
+        for (int v = 4; v < NV; ++v) l4[v & 3] += e[qb][v];
+      }
       ls[qb] = (l4[0] + l4[1]) + (l4[2] + l4[3]);
     }
   };
   float e[QB][NV], ls[QB], sh[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) sh[qb] = 0.f;
-  exp2_all(e, sh);
-  __builtin_amdgcn_sched_barrier(0);
-  row_sums(e, ls);
-  bool need = false;
+  for (int qb = 0; qb < QB; ++qb) {
+    sh[qb] = 0.f;
+    alpha[qb] = 1.f;
+  }
+  any = false;
+  // One pass in the common case.  A second pass, after the maxima moved the
+  // reference, recomputes P and its sums with the same code (a single
+  // definition of P keeps register use as in one pass).
+  bool again = false;
+#pragma nounroll
+  for (;;) {
+    exp2_all(e, sh);
+    __builtin_amdgcn_sched_barrier(0);
+    pack_sums(e, ls);
+    if (again) break;
+    bool need = false;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-    need = need || (!STEADY && mprev[qb] == -__builtin_inff()) || !(ls[qb] <= psum_max);
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
-    any = false;
+    for (int qb = 0; qb < QB; ++qb)
+      need = need || (!STEADY && mprev[qb] == -__builtin_inff()) || !(ls[qb] <= psum_max);
+    if (__builtin_amdgcn_ballot_w64(need) == 0) break;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float m4[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
@@ -660,20 +714,16 @@ __device__ __forceinline__ void softmax_tail(WaveState<TL>& ws, float (&alpha)[T
       ws.m[qb] = mnew;
       sh[qb] = mref - mu[qb];
     }
-    exp2_all(e, sh);
-    __builtin_amdgcn_sched_barrier(0);
-    row_sums(e, ls);
-  } else {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) alpha[qb] = 1.f;
-    any = false;
+    again = true;
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     ws.l[qb] = ws.l[qb] * alpha[qb] + ls[qb];
+    if (!Mma<T>::PACKED_SUMS) {
 #pragma unroll
-    for (int w = 0; w < NV / 2; ++w)
-      pfr[qb][w / 8][w % 8] = Mma<T>::pack(e[qb][2 * w], e[qb][2 * w + 1]);
+      for (int w = 0; w < NV / 2; ++w)
+        pfr[qb][w / 8][w % 8] = Mma<T>::pack(e[qb][2 * w], e[qb][2 * w + 1]);
+    }
   }
   // O has received P·V of tile i-1 and not yet that of tile i.
   if (any) rescale_o(ws, alpha);
