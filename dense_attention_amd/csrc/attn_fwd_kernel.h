@@ -193,7 +193,9 @@ struct Tile {
 // (wait_vmem) before the workgroup barrier that publishes a tile, and no LDS
 // location is read while a copy into it is in flight.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const lds_t* lds) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)lds;
+  // Wave-uniform by construction; readfirstlane keeps it in an SGPR where the
+  // compiler cannot prove that (it is a no-op on an SGPR value).
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
@@ -281,6 +283,14 @@ struct DmaPlan {
 __device__ __forceinline__ void wait_vmem() {
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
   __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// s_waitcnt vmcnt(N): all but the N most recent vector memory operations of
+// the wave have completed (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ u32x4_t ld_global16(const uint16_t* p) {
@@ -392,8 +402,13 @@ struct Ring {
 
 template <class TL>
 struct Copies {
-  DmaPlan<TL, TL::KS, true> k;
-  DmaPlan<TL, TL::VS, false, (TL::BN * TL::KS / 1024) % TL::GW, TL::VSWZ> v;
+  using KPlan = DmaPlan<TL, TL::KS, true>;
+  using VPlan = DmaPlan<TL, TL::VS, false, (TL::BN * TL::KS / 1024) % TL::GW, TL::VSWZ>;
+  KPlan k;
+  VPlan v;
+  // Copy instructions every wave issues for one K tile plus one V tile (at
+  // least; waves differ by one where the blocks do not divide evenly).
+  static constexpr int MIN_ISSUED = KPlan::BLOCKS / TL::GW + VPlan::BLOCKS / TL::GW;
 };
 
 // Epilogue of a work item: O / l (rounded to the output type, or fp32 for a
@@ -957,12 +972,21 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   //    issued in V(i) overwrites K_{i-1} and V_{i-2} (read in M(i-1), which
   //    ends before V(i) of either group starts); c(i+2) issued by group 1 in
   //    slot 2i+2 overwrites K_i and V_{i-1}, read in slots 2i and 2i+1.
+  //  * three-deep shared ring, group 1 (G1A3): ahead = 3.  Its V(i) falls in
+  //    slot 2i+2, and c(i+3) overwrites K_i and V_{i-1}, read in M(i) of both
+  //    groups (slots 2i and 2i+1).  At the end of its M(i) (slot 2i+1) it
+  //    needs its share of c(i+1), issued in slot 2i-2; in the steady loop it
+  //    waits only for that, letting the share of c(i+2) issued since stay in
+  //    flight (with ahead = 2 the share of c(i+1) would have been issued one
+  //    slot before, and the wait showed at that barrier).
   // No DMA is issued or awaited inside a leading MFMA phase.
-  const int ahead = (DEEP || !lead) ? 2 : 1;
+  constexpr bool G1A3 = TL::STAGES == 3 && !TL::KSPLIT && TL::NW == 8;
+  const int ahead = (!lead && G1A3) ? 3 : (DEEP || !lead) ? 2 : 1;
   SAcc<TL> sacc;
   PFrag<TL> pfr;
   if (grp == 1) {  // group 1 sits out slot 0
     if (!lead && !DEEP) copy_set(1);
+    if (!lead && G1A3) copy_set(2);
     __syncthreads();
   }
   // Softmax state handed from M(i) to V(i): rescale factors, the maximum
@@ -996,8 +1020,10 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
     step(0, [&]() { copy_set(ahead); }, masked(0));
     // Steps 1 .. steady copy only whole tiles and softmax unmasked tiles; the
     // remaining (at least the last three) steps are peeled so the steady loop
-    // carries no such branches.
-    const int steady = CAUSAL ? min(ntg - 4, t_mask - tb - 1) : ntg - 4;
+    // carries no such branches.  A schedule that copies three tiles ahead
+    // stops one step earlier: its step ntg-4 copies the last, maybe ragged,
+    // tile.  (Every step passes the same two barriers, steady or peeled.)
+    const int steady = (CAUSAL ? min(ntg - 4, t_mask - tb - 1) : ntg - 4) - (ahead == 3 ? 1 : 0);
     // Steady step i.  With copies two tiles ahead the loop is unrolled by the
     // ring depth, so every ring buffer a step touches (K_i, V_{i-1}, and the
     // copy targets K_{i+2}, V_{i+1}) is a compile-time offset: RR carries
@@ -1010,12 +1036,18 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
       lds_t* const k_i = R >= 0 ? ring.base + R * TL::K_TILE : ring.k(i);
       lds_t* const v_im1 = R >= 0 ? vbase + ((R + NS - 1) % NS) * TL::V_TILE : ring.v(i - 1);
       mma_phase<T, TL, true, true, true>(ws, k_i, v_im1, sacc, pfr, mprev, mu, c, lane);
-      if (!lead) wait_vmem();
+      if (!lead) {
+        // Steady steps issue whole copy sets, so all but the most recent one
+        // are complete once no more than one set's instructions are pending.
+        if (G1A3) wait_vmem_n<Copies<TL>::MIN_ISSUED>();
+        else wait_vmem();
+      }
       __syncthreads();
       if (DEEP && lead) wait_vmem();
-      const int j = i + ahead;  // compile-time slots only occur with ahead == 2 (DEEP)
-      lds_t* const k_j = R >= 0 ? ring.base + ((R + 2) % NS) * TL::K_TILE : ring.k(j);
-      lds_t* const v_jm1 = R >= 0 ? vbase + ((R + 1) % NS) * TL::V_TILE : ring.v(j - 1);
+      const int j = i + ahead;  // compile-time slots only occur with ahead 2 or 3 (DEEP)
+      const int rj = (!lead && G1A3) ? (R + 3) % NS : (R + 2) % NS;
+      lds_t* const k_j = R >= 0 ? ring.base + rj * TL::K_TILE : ring.k(j);
+      lds_t* const v_jm1 = R >= 0 ? vbase + ((rj + NS - 1) % NS) * TL::V_TILE : ring.v(j - 1);
       cp.k.issue(kh + (long long)(j * BN) * kss, k_j, qw);
       cp.v.issue(vh + (long long)((j - 1) * BN) * vss, v_jm1, qw);
       softmax_tail<T, TL, false, CAUSAL, true>(ws, alpha, any, sacc, pfr, mprev, mu, i * BN, klg, thr,
