@@ -243,7 +243,10 @@ int attn_merge(const float* o_parts, const float* lse_parts, int n_parts, void* 
  * into `kv_splits` ranges processed by separate workgroups, then merged: more
  * independent work items when B·H·ceil(S/block_m) would leave compute units
  * idle.  One launch computes all partials into `workspace`, a second merges
- * them into o and lse.
+ * them into o and lse.  ("Learning FlashAttention the Hard Way - Part 2",
+ * "Wrap-Up": the running (max, sum, output) carrier of a key range is
+ * associative, which is what licenses splitting the key axis across
+ * workgroups; its References name split-KV as the split-K of that carrier.)
  *
  *   kv_splits        >= 1, or 0 for the library's choice (enough items to
  *                    fill every compute unit, each range at least 256 keys).
