@@ -161,7 +161,19 @@ struct Tile {
   // K/V ring depth: three tiles when they fit in LDS, else two.
   static constexpr int STAGES = 3 * RINGS * (BN * (KS + VS)) <= 160 * 1024 ? 3 : 2;
   static constexpr int RING_BYTES = STAGES * (K_TILE + V_TILE);
-  static constexpr int LDS_BYTES = RINGS * RING_BYTES;
+  // 16-bit O rows leave through LDS where there is room (STAGE_O): each wave
+  // writes its rows there in the accumulator layout and reads them back as
+  // whole rows, so a store instruction covers a few full rows instead of 32
+  // bytes of 32 rows.  The staging area starts at V slot 1, which the next
+  // item's first copies (K slots 0-1, V slot 0) never target; its rows are
+  // padded by 16 bytes so that the accumulator-layout writes spread over
+  // the banks.
+  static constexpr int SROW = D * 2 + 16;
+  static constexpr int STAGE_OFF = STAGES * K_TILE + V_TILE;
+  static constexpr int STAGE_END = STAGE_OFF + NW * QB * 32 * SROW;
+  static constexpr bool STAGE_O = !KSPLIT && STAGES == 3 && STAGE_END <= 160 * 1024;
+  static constexpr int LDS_BYTES =
+      STAGE_O && STAGE_END > RINGS * RING_BYTES ? STAGE_END : RINGS * RING_BYTES;
   // Per-lane 16-byte chunks one wave hands over in the key-split merge: the
   // O accumulators, then (m, l) of each query block.
   static constexpr int XCH = QB * (D / 32) * 4 + 1;
@@ -412,21 +424,45 @@ struct Copies {
 };
 
 // Epilogue of a work item: O / l (rounded to the output type, or fp32 for a
-// partial result over one KV range) and the LSE.
+// partial result over one KV range) and the LSE.  With STAGE_O, 16-bit rows
+// go through the wave's own part of the LDS staging area: every ring read of
+// the item is over (the item's final barriers), and the next item writes the
+// area only after the barrier that starts its loop.
 template <class T, class TL>
 __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL>& ws,
-                                             long long o_off, long long lse_off, int qt, int qw,
-                                             int lane) {
+                                             lds_t* smem, long long o_off, long long lse_off,
+                                             int qt, int qw, int lane) {
   constexpr int QB = TL::QB, DB = TL::D / 32;
   const int lr = lane & 31;
   const int hh = lane >> 5;
+  const bool staged = TL::STAGE_O && !p.o_f32;
+  lds_t* const stage = smem + TL::STAGE_OFF + qw * QB * 32 * TL::SROW;
+  // Columns db·32 + 16·hh + [0, 8) and [8, 16) of the lane's row, rounded.
+  auto pack16 = [&](int qb, int db, float inv, u32x4_t& w0, u32x4_t& w1) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = Mma<T>::pack(ws.o[qb][db][2 * i] * inv, ws.o[qb][db][2 * i + 1] * inv);
+    w0 = u32x4_t{w[0], w[1], w[2], w[3]};
+    w1 = u32x4_t{w[4], w[5], w[6], w[7]};
+  };
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lane_pair_sum(ws.l[qb]);
     const int row = qt * TL::BM + (qw * QB + qb) * 32 + lr;
+    // lt == 0 only for a row without any valid key (causal): O = 0, LSE = -inf.
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    if (staged) {
+      lds_t* srow = stage + (qb * 32 + lr) * TL::SROW;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x4_t w0, w1;
+        pack16(qb, db, inv, w0, w1);
+        st_lds16(srow + db * 64 + 32 * hh, w0);
+        st_lds16(srow + db * 64 + 32 * hh + 16, w1);
+      }
+    }
     if (row < p.Sq) {
-      // lt == 0 only for a row without any valid key (causal): O = 0, LSE = -inf.
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       const long long ro = o_off + (long long)row * p.o_ss;
       if (p.o_f32) {
         float* orow = static_cast<float*>(p.o) + ro;
@@ -439,16 +475,12 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
             for (int e = 0; e < 4; ++e) w[e] = f2u(ws.o[qb][db][4 * j + e] * inv);
             *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh + 4 * j) = w;
           }
-      } else {
+      } else if (!staged) {
         uint16_t* orow = static_cast<uint16_t*>(p.o) + ro;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          uint32_t w[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            w[i] = Mma<T>::pack(ws.o[qb][db][2 * i] * inv, ws.o[qb][db][2 * i + 1] * inv);
-          u32x4_t w0 = {w[0], w[1], w[2], w[3]};
-          u32x4_t w1 = {w[4], w[5], w[6], w[7]};
+          u32x4_t w0, w1;
+          pack16(qb, db, inv, w0, w1);
           *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh) = w0;
           *reinterpret_cast<u32x4_t*>(orow + db * 32 + 16 * hh + 8) = w1;
         }
@@ -458,6 +490,26 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
         p.lse[lse_off + row] = lt > 0.f ? (ws.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f
                                         : -__builtin_inff();
       }
+    }
+  }
+  if (staged) {
+    // Read back as whole rows: 16-byte chunk i·64 + lane of the wave's rows.
+    constexpr int CPR = TL::D / 8;
+    constexpr int NRD = QB * 32 * CPR / 64;
+    static_assert(QB * 32 * CPR % 64 == 0, "staged rows fill whole instructions");
+    const int row0 = qt * TL::BM + qw * QB * 32;
+    uint16_t* const ob = static_cast<uint16_t*>(p.o) + o_off;
+    u32x4_t x[NRD];
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) {
+      const int ch = i * 64 + lane;
+      x[i] = ld_lds16(stage + (ch / CPR) * TL::SROW + (ch % CPR) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) {
+      const int ch = i * 64 + lane;
+      const int r = row0 + ch / CPR;
+      if (r < p.Sq) *reinterpret_cast<u32x4_t*>(ob + (long long)r * p.o_ss + (ch % CPR) * 8) = x[i];
     }
   }
 }
@@ -493,49 +545,47 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<TL
 // operands are read from LDS two slots ahead, and scheduling barriers keep
 // every slot's work in place.
 
-// STEADY: a step of the steady loop, where every row's kept maximum is already
-// finite (tile 0 of the item, or of the group, was visible to every row), so
-// the guards for m = -inf are left out.
-template <class T, class TL, bool QK, bool PV, bool STEADY = false>
-__device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
-                                          SAcc<TL>& sacc, const PFrag<TL>& pfr,
-                                          float (&mprev)[TL::QB], float (&mu)[TL::QB], float c,
-                                          int lane) {
-  constexpr int QB = TL::QB, NB = TL::BN / 32, DT = TL::D / 16, DB = TL::D / 32;
-  constexpr int NQ = QK ? NB * DT : 0;   // Sᵀ MFMAs (slots 0 .. NQ-1)
-  constexpr int NP = PV ? NB * 2 * DB : 0;  // P·V MFMAs (slots NQ .. NS-1)
-  constexpr int NS = NQ + NP;
-  constexpr int NV = NB * 16;            // scores per lane per 32-query block
-  static_assert(NS >= 1, "empty phase");
+// LDS operands of an MFMA phase.  Slot s reads a K fragment for an Sᵀ MFMA
+// (key block s % NB, head-dim step s / NB) or a V fragment for a P·V MFMA:
+// lane group g = lane/16 covers key half g/2 and head-dim half g%2; inside
+// the group, lane i reads key row i/4 and the 8-byte piece of head-dim
+// columns chosen so that the transposed result is lane_key-ordered.  Slot
+// order: all Sᵀ slots then all P·V slots, or with ALT (and both kinds
+// present) Sᵀ in the even slots and P·V in the odd ones.
+template <class TL, bool QK, bool PV>
+struct Operands {
+  static constexpr int NB = TL::BN / 32, DT = TL::D / 16, DB = TL::D / 32;
+  static constexpr int NQ = QK ? NB * DT : 0;       // Sᵀ MFMAs
+  static constexpr int NP = PV ? NB * 2 * DB : 0;   // P·V MFMAs
+  static constexpr int NS = NQ + NP;
+  static constexpr bool IL = TL::ALT && QK && PV && NQ == NP;
+  static constexpr bool is_qk(int s) { return IL ? s % 2 == 0 : s < NQ; }
+  static constexpr int qk_index(int s) { return IL ? s / 2 : s; }
+  static constexpr int pv_index(int s) { return IL ? s / 2 : s - NQ; }
+  const lds_t* kbase;
+  const lds_t* vbase;
+  const lds_t* vbase1;
 
-  const int g = lane >> 4;
-  const int li = lane & 15;
-  uint32_t ka = (uint32_t)(uintptr_t)kl + (uint32_t)((lane & 31) * TL::KS + (lane >> 5) * 16);
-  const int vrow = 16 * (g >> 1) + (li >> 2);
-  int vchunk = 2 * (li & 1) + (g & 1);
-  if (TL::VSWZ) vchunk ^= ((vrow >> 1) & 1) << 2;
-  uint32_t va = (uint32_t)(uintptr_t)vl + (uint32_t)(vrow * TL::VS + vchunk * 16 + ((li >> 1) & 1) * 8);
-  // Swizzled V: the second 64 bytes of a row (db = 1) sit at the address with
-  // bit 6 flipped, which no immediate offset expresses; a second base.
-  uint32_t va1 = va ^ 64u;
-  if (QK) asm volatile("" : "+v"(ka));
-  if (PV) asm volatile("" : "+v"(va));
-  if (PV && TL::VSWZ) asm volatile("" : "+v"(va1));
-  const lds_t* kbase = (const lds_t*)(uintptr_t)ka;
-  const lds_t* vbase = (const lds_t*)(uintptr_t)va;
-  const lds_t* vbase1 = (const lds_t*)(uintptr_t)va1;
-  // Operand of slot s: a K fragment for an Sᵀ MFMA (key block s % NB, head-dim
-  // step s / NB) or a V fragment for a P·V MFMA: lane group g = lane/16
-  // covers key half g/2 and head-dim half g%2; inside the group, lane i reads
-  // key row i/4 and the 8-byte piece of head-dim columns chosen so that the
-  // transposed result is lane_key-ordered.
-  // Slot order: all Sᵀ slots then all P·V slots, or with ALT (and both kinds
-  // present) Sᵀ in the even slots and P·V in the odd ones.
-  constexpr bool IL = TL::ALT && QK && PV && NQ == NP;
-  auto is_qk = [](int s) { return IL ? s % 2 == 0 : s < NQ; };
-  auto qk_index = [](int s) { return IL ? s / 2 : s; };
-  auto pv_index = [](int s) { return IL ? s / 2 : s - NQ; };
-  auto frag = [&](int s) -> u32x4_t {
+  __device__ __forceinline__ Operands(const lds_t* kl, const lds_t* vl, int lane) {
+    const int g = lane >> 4;
+    const int li = lane & 15;
+    uint32_t ka = (uint32_t)(uintptr_t)kl + (uint32_t)((lane & 31) * TL::KS + (lane >> 5) * 16);
+    const int vrow = 16 * (g >> 1) + (li >> 2);
+    int vchunk = 2 * (li & 1) + (g & 1);
+    if (TL::VSWZ) vchunk ^= ((vrow >> 1) & 1) << 2;
+    uint32_t va = (uint32_t)(uintptr_t)vl + (uint32_t)(vrow * TL::VS + vchunk * 16 + ((li >> 1) & 1) * 8);
+    // Swizzled V: the second 64 bytes of a row (db = 1) sit at the address
+    // with bit 6 flipped, which no immediate offset expresses; a second base.
+    uint32_t va1 = va ^ 64u;
+    if (QK) asm volatile("" : "+v"(ka));
+    if (PV) asm volatile("" : "+v"(va));
+    if (PV && TL::VSWZ) asm volatile("" : "+v"(va1));
+    kbase = (const lds_t*)(uintptr_t)ka;
+    vbase = (const lds_t*)(uintptr_t)va;
+    vbase1 = (const lds_t*)(uintptr_t)va1;
+  }
+
+  __device__ __forceinline__ u32x4_t frag(int s) const {
     if (is_qk(s)) {
       const int q = qk_index(s);
       return ld_lds16(kbase + (q % NB) * 32 * TL::KS + (q / NB) * 32);
@@ -548,12 +598,29 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
     const u32x2_t hi = ld_lds_tr(pv0 + 4 * TL::VS);
     const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
     return a;
-  };
+  }
+};
+
+// STEADY: a step of the steady loop, where every row's kept maximum is already
+// finite (tile 0 of the item, or of the group, was visible to every row), so
+// the guards for m = -inf are left out.
+template <class T, class TL, bool QK, bool PV, bool STEADY = false>
+__device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, const lds_t* vl,
+                                          SAcc<TL>& sacc, const PFrag<TL>& pfr,
+                                          float (&mprev)[TL::QB], float (&mu)[TL::QB], float c,
+                                          int lane) {
+  using Op = Operands<TL, QK, PV>;
+  constexpr int QB = TL::QB, NB = Op::NB, DB = Op::DB;
+  constexpr int NQ = Op::NQ, NP = Op::NP, NS = Op::NS;
+  constexpr int NV = NB * 16;            // scores per lane per 32-query block
+  static_assert(NS >= 1, "empty phase");
+  constexpr bool IL = Op::IL;
+  const Op op(kl, vl, lane);
   constexpr int LD = 2;  // operands are read two slots ahead
   if (TL::PRIO) __builtin_amdgcn_s_setprio(3);
   u32x4_t fr[NS];
 #pragma unroll
-  for (int j = 0; j < LD && j < NS; ++j) fr[j] = frag(j);
+  for (int j = 0; j < LD && j < NS; ++j) fr[j] = op.frag(j);
 
   // First half of the softmax of the new Sᵀ: x = s·c - mu in place, one unit
   // per score.  mu is the kept maximum m (0 while m is still -inf, so that no
@@ -584,14 +651,14 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
   const f32x16_t zero = {};
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (is_qk(s)) {
-      const int q = qk_index(s);
+    if (Op::is_qk(s)) {
+      const int q = Op::qk_index(s);
       const int nb = q % NB, t = q / NB;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         sacc[qb][nb] = Mma<T>::mfma(fr[s], ws.qf[qb][t], t == 0 ? zero : sacc[qb][nb]);
     } else {
-      const int i = pv_index(s);
+      const int i = Op::pv_index(s);
       const int nb = i / (2 * DB), mm = (i / DB) % 2, db = i % DB;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -600,7 +667,7 @@ __device__ __forceinline__ void mma_phase(WaveState<TL>& ws, const lds_t* kl, co
         ws.o[qb][db] = Mma<T>::mfma(fr[s], b, ws.o[qb][db]);
       }
     }
-    if (s + LD < NS) fr[s + LD] = frag(s + LD);
+    if (s + LD < NS) fr[s + LD] = op.frag(s + LD);
     if (!IL && SLOTS > 0 && s >= FIRST) {
       // Slot FIRST + j takes units u with floor(u·SLOTS/NU) == j.
       const int j = s - FIRST;
@@ -808,14 +875,150 @@ __device__ __forceinline__ void merge_key_halves(WaveState<TL>& ws, lds_t* smem,
   __syncthreads();
 }
 
-template <class T, class TL, bool CAUSAL>
-__device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& cp, lds_t* smem,
-                                             int item, int wave, int lane) {
-  constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, DB = D / 32, DT = D / 16;
+// Geometry of one work item as one wave sees it: item -> (KV range sp, head
+// bh, query tile qt), the keys the item sees, and this wave group's share.
+struct ItemGeom {
+  int qt, bh, sp, b, h, k0, S, nt, t_mask, klim, nt0, tb, ntg, Sg, klg;
+  bool ragged;
+  const uint16_t* qh;
+  const uint16_t* kh;
+  const uint16_t* vh;
+};
+
+template <class TL, bool CAUSAL>
+__device__ __forceinline__ ItemGeom item_geom(const Params& p, int item, int grp, int qw, int lr) {
+  constexpr int BN = TL::BN;
   constexpr bool KSPLIT = TL::KSPLIT;
-  static_assert(!CAUSAL || QB == 1, "causal masks assume one 32-query block per wave");
+  ItemGeom g;
+  // Non-causal: consecutive items are the query tiles of one head and one KV
+  // range.  Causal: the last (longest) query tiles of every head come first,
+  // so that workgroups dispatched in order start with the largest items;
+  // consecutive items are different heads, and head bh lands on XCD bh % 8
+  // when B·H % 8 == 0.
+  int t_;
+  if (CAUSAL) {
+    g.bh = item % p.BH;
+    t_ = item / p.BH;
+    g.qt = p.n_qtiles - 1 - t_ % p.n_qtiles;
+    g.sp = t_ / p.n_qtiles;
+  } else {
+    g.qt = item % p.n_qtiles;
+    t_ = item / p.n_qtiles;
+    g.bh = t_ % p.BH;
+    g.sp = t_ / p.BH;
+  }
+  g.b = g.bh / p.H;
+  g.h = g.bh - g.b * p.H;
+  g.k0 = g.sp * p.split_len;
+  // S (keys of this item's range) passes through an empty asm so that per-lane
+  // values derived from it (tail masks, clamped copy addresses) are recomputed
+  // per item instead of being hoisted out of the persistent loop, where they
+  // would occupy registers for the whole kernel.
+  int S = min(p.Skv - g.k0, p.split_len);
+  asm volatile("" : "+s"(S));
+  g.S = S;
+  g.qh = p.q + g.b * p.q_sb + g.h * p.q_sh;
+  // Keys of the range visible to this item: all S, or with a causal mask the
+  // prefix that its last query row sees.  Whole tiles below t_mask are
+  // visible to every row of the item and carry no mask.
+  g.klim = S;  // this lane's key limit, counted from the range start
+  if (CAUSAL) {
+    const int q_first = g.qt * TL::BM;
+    const int q_last = min(p.Sq, q_first + TL::BM) - 1;
+    const int seen = min(S, q_last + p.coff - g.k0 + 1);
+    g.nt = seen > 0 ? (seen + BN - 1) / BN : 0;
+    g.t_mask = min(max(q_first + p.coff - g.k0 + 1, 0), S) / BN;
+    const int row = q_first + qw * 32 + lr;
+    g.klim = min(S, max(row + p.coff - g.k0 + 1, 0));
+  } else {
+    g.nt = (S + BN - 1) / BN;
+    g.t_mask = S / BN;
+  }
+  g.ragged = (S % BN) != 0;
+  // This group's tiles: all nt, or with a key split the first ceil(nt/2)
+  // (group 0) or the rest (group 1, starting at tile tb).  Sg and klg count
+  // keys from the group's first tile.
+  g.nt0 = KSPLIT ? (g.nt + 1) / 2 : g.nt;
+  g.tb = (KSPLIT && grp == 1) ? g.nt0 : 0;
+  g.ntg = (KSPLIT && grp == 1) ? g.nt - g.nt0 : g.nt0;
+  g.Sg = S - g.tb * BN;
+  g.klg = g.klim - g.tb * BN;
+  g.kh = p.k + g.b * p.k_sb + g.h * p.k_sh + (long long)(g.k0 + g.tb * BN) * p.k_ss;
+  g.vh = p.v + g.b * p.v_sb + g.h * p.v_sh + (long long)(g.k0 + g.tb * BN) * p.v_ss;
+  return g;
+}
+
+// Copy set c(t) = {K_t, V_{t-1}} of an item: the tiles M(t) reads.  Each wave
+// issues its share; tiles that run past the group's last key are clamped.
+template <class TL>
+__device__ __forceinline__ void issue_copy_set(const Params& p, const Copies<TL>& cp,
+                                               const ItemGeom& g, const Ring<TL>& ring, int t,
+                                               int qw, int lane) {
+  constexpr int BN = TL::BN;
+  if (t < g.ntg) {
+    const uint16_t* kt = g.kh + (long long)(t * BN) * p.k_ss;
+    if ((t + 1) * BN <= g.Sg)
+      cp.k.issue(kt, ring.k(t), qw);
+    else
+      cp.k.issue_clamped(kt, g.Sg - t * BN, (uint32_t)p.k_ss * 2u, ring.k(t), qw, lane);
+  }
+  if (t >= 1 && t <= g.ntg) {
+    const int u = t - 1;
+    const uint16_t* vt = g.vh + (long long)(u * BN) * p.v_ss;
+    if ((u + 1) * BN <= g.Sg)
+      cp.v.issue(vt, ring.v(u), qw);
+    else
+      cp.v.issue_clamped(vt, g.Sg - u * BN, (uint32_t)p.v_ss * 2u, ring.v(u), qw, lane);
+  }
+}
+
+// Prologue of an item: c(0) (and with copies two tiles ahead, on three-deep
+// rings and on every key-split ring, c(1)) and the wave's Q rows into the
+// MFMA B-operand registers.  Rows past Sq load row Sq-1 instead: they are
+// computed on that copy and never stored, and the loads need no lane mask
+// (a masked load into zeroed registers made the compiler wait for every
+// vector memory operation in flight, the copies just issued included).
+template <class TL>
+__device__ __forceinline__ void item_prologue(const Params& p, const Copies<TL>& cp,
+                                              const ItemGeom& g, const Ring<TL>& ring,
+                                              WaveState<TL>& ws, int qw, int lane) {
+  constexpr bool DEEP = TL::STAGES == 3 || TL::KSPLIT;
+  constexpr int QB = TL::QB, DT = TL::D / 16;
+  if (g.ntg > 0) {
+    issue_copy_set<TL>(p, cp, g, ring, 0, qw, lane);
+    if (DEEP) issue_copy_set<TL>(p, cp, g, ring, 1, qw, lane);
+  }
   const int lr = lane & 31;
   const int hh = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = min(g.qt * TL::BM + (qw * QB + qb) * 32 + lr, p.Sq - 1);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) ws.qf[qb][t] = ld_global16(g.qh + (long long)row * p.q_ss + 16 * t + 8 * hh);
+  }
+}
+
+// One work item.  `pre` < 0: the item's prologue is issued here; otherwise the
+// previous item already issued it ahead of its own O stores, and `pre` is the
+// number of those stores that may still be in flight when the prologue's
+// copies and Q rows have landed (vector memory operations complete in issue
+// order).  With a next item (non-causal persistent grids), this item issues
+// the next one's prologue once its own K/V reads are over, ahead of its
+// stores, and returns the `pre` for it; otherwise it returns -1.  All work
+// items reach their ends at about the same time, so their O stores form one
+// burst of HBM writes: the next item's copies and Q rows no longer queue
+// behind it, and the stores drain during the next item's first slots.
+template <class T, class TL, bool CAUSAL>
+__device__ __forceinline__ int process_item(const Params& p, const Copies<TL>& cp, lds_t* smem,
+                                            int item, int next, int wave, int lane,
+                                            WaveState<TL>& ws, int pre) {
+  constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, DB = D / 32;
+  constexpr bool KSPLIT = TL::KSPLIT;
+  // O stores of a wave whose rows are all below Sq (at least; more with fp32
+  // partials or the LSE).
+  constexpr int NST = QB * DB * 2;
+  static_assert(!CAUSAL || QB == 1, "causal masks assume one 32-query block per wave");
+  const int lr = lane & 31;
   // Wave groups: waves w and w+4 share a SIMD.  grp decides the slot offset
   // of the ping-pong schedule.  Without a key split the groups hold different
   // query rows and consume one K/V stream, whose copies they share; group 1
@@ -825,127 +1028,43 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
   const int grp = TL::NW == 8 ? (wave >> 2) : 0;
   const int qw = KSPLIT ? (wave & 3) : wave;
   const bool lead = KSPLIT || grp == 0;
-  // Item -> (KV range sp, head bh, query tile qt).  Non-causal: consecutive
-  // items are the query tiles of one head and one KV range.  Causal: the
-  // last (longest) query tiles of every head come first, so that workgroups
-  // dispatched in order start with the largest items; consecutive items are
-  // different heads, and head bh lands on XCD bh % 8 when B·H % 8 == 0.
-  int qt, t_, bh, sp;
-  if (CAUSAL) {
-    bh = item % p.BH;
-    t_ = item / p.BH;
-    qt = p.n_qtiles - 1 - t_ % p.n_qtiles;
-    sp = t_ / p.n_qtiles;
-  } else {
-    qt = item % p.n_qtiles;
-    t_ = item / p.n_qtiles;
-    bh = t_ % p.BH;
-    sp = t_ / p.BH;
-  }
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
-  const int k0 = sp * p.split_len;
-  // S (keys of this item's range) passes through an empty asm so that per-lane
-  // values derived from it (tail masks, clamped copy addresses) are recomputed
-  // per item instead of being hoisted out of the persistent loop, where they
-  // would occupy registers for the whole kernel.
-  int S = min(p.Skv - k0, p.split_len);
-  asm volatile("" : "+s"(S));
+  const ItemGeom g = item_geom<TL, CAUSAL>(p, item, grp, qw, lr);
+  const int qt = g.qt, bh = g.bh, sp = g.sp, b = g.b, h = g.h;
+  const int nt = g.nt, t_mask = g.t_mask;
+  const bool ragged = g.ragged;
   const float c = p.c, thr = p.thr;
   // A lane's partial row sum of p = 2^(s·c - m) up to this bound proves that
   // none of its scores exceeds m + thr (see softmax_tail).
   const float psum_max = __builtin_amdgcn_exp2f(thr);
   const int kss = p.k_ss, vss = p.v_ss;
-  const uint32_t krb = (uint32_t)kss * 2u, vrb = (uint32_t)vss * 2u;
 
-  const uint16_t* __restrict__ qh = p.q + b * p.q_sb + h * p.q_sh;
-  // Keys of the range visible to this item: all S, or with a causal mask the
-  // prefix that its last query row sees.  Whole tiles below t_mask are
-  // visible to every row of the item and carry no mask.
-  int nt, t_mask;
-  int klim = S;  // this lane's key limit, counted from the range start
-  if (CAUSAL) {
-    const int q_first = qt * TL::BM;
-    const int q_last = min(p.Sq, q_first + TL::BM) - 1;
-    const int seen = min(S, q_last + p.coff - k0 + 1);
-    nt = seen > 0 ? (seen + BN - 1) / BN : 0;
-    t_mask = min(max(q_first + p.coff - k0 + 1, 0), S) / BN;
-    const int row = q_first + qw * 32 + lr;
-    klim = min(S, max(row + p.coff - k0 + 1, 0));
-  } else {
-    nt = (S + BN - 1) / BN;
-    t_mask = S / BN;
-  }
-  const bool ragged = (S % BN) != 0;
   if (CAUSAL && nt == 0) {
     // No query row of this item sees a key of the range: O = 0, LSE = -inf.
-    if (KSPLIT && grp == 1) return;
-    WaveState<TL> ws;
+    if (KSPLIT && grp == 1) return -1;
+    WaveState<TL> wz;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      ws.m[qb] = -__builtin_inff();
-      ws.l[qb] = 0.f;
+      wz.m[qb] = -__builtin_inff();
+      wz.l[qb] = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ws.o[qb][db][i] = 0.f;
+        for (int i = 0; i < 16; ++i) wz.o[qb][db][i] = 0.f;
     }
-    store_output<T, TL>(p, ws, sp * p.o_split + b * p.o_sb + h * p.o_sh,
+    store_output<T, TL>(p, wz, smem, sp * p.o_split + b * p.o_sb + h * p.o_sh,
                        sp * p.lse_split + (long long)bh * p.Sq, qt, qw, lane);
-    return;
+    return -1;
   }
 
-  // This group's tiles: all nt, or with a key split the first ceil(nt/2)
-  // (group 0) or the rest (group 1, starting at tile tb).  Sg and klg count
-  // keys from the group's first tile.
-  const int nt0 = KSPLIT ? (nt + 1) / 2 : nt;
-  const int tb = (KSPLIT && grp == 1) ? nt0 : 0;
-  const int ntg = (KSPLIT && grp == 1) ? nt - nt0 : nt0;
-  const int Sg = S - tb * BN;
-  const int klg = klim - tb * BN;
-  const uint16_t* __restrict__ kh = p.k + b * p.k_sb + h * p.k_sh + (long long)(k0 + tb * BN) * kss;
-  const uint16_t* __restrict__ vh = p.v + b * p.v_sb + h * p.v_sh + (long long)(k0 + tb * BN) * vss;
+  const int nt0 = g.nt0, tb = g.tb, ntg = g.ntg, klg = g.klg;
+  const uint16_t* __restrict__ kh = g.kh;
+  const uint16_t* __restrict__ vh = g.vh;
   const Ring<TL> ring{smem + (KSPLIT ? grp * TL::RING_BYTES : 0)};
-
-  // Copy set c(t) = {K_t, V_{t-1}}: the tiles M(t) reads.  Each wave issues its
-  // share; tiles that run past the last key are clamped.
-  auto copy_k = [&](int t) {
-    const uint16_t* kt = kh + (long long)(t * BN) * kss;
-    if ((t + 1) * BN <= Sg)
-      cp.k.issue(kt, ring.k(t), qw);
-    else
-      cp.k.issue_clamped(kt, Sg - t * BN, krb, ring.k(t), qw, lane);
-  };
-  auto copy_v = [&](int t) {
-    const uint16_t* vt = vh + (long long)(t * BN) * vss;
-    if ((t + 1) * BN <= Sg)
-      cp.v.issue(vt, ring.v(t), qw);
-    else
-      cp.v.issue_clamped(vt, Sg - t * BN, vrb, ring.v(t), qw, lane);
-  };
-  auto copy_set = [&](int t) {
-    if (t < ntg) copy_k(t);
-    if (t >= 1 && t <= ntg) copy_v(t - 1);
-  };
-
-  // Prologue: c(0) (and with copies two tiles ahead, c(1)) in flight while Q
-  // is loaded into registers.  DEEP: copies run two tiles ahead, on three-deep
-  // rings and on every key-split ring (see below).
+  auto copy_set = [&](int t) { issue_copy_set<TL>(p, cp, g, ring, t, qw, lane); };
   constexpr bool DEEP = TL::STAGES == 3 || TL::KSPLIT;
-  if (ntg > 0) {
-    copy_set(0);
-    if (DEEP) copy_set(1);
-  }
-  WaveState<TL> ws;
+  if (pre < 0) item_prologue<TL>(p, cp, g, ring, ws, qw, lane);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = qt * TL::BM + (qw * QB + qb) * 32 + lr;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (row < p.Sq) x = ld_global16(qh + (long long)row * p.q_ss + 16 * t + 8 * hh);
-      ws.qf[qb][t] = x;
-    }
     ws.m[qb] = -__builtin_inff();
     ws.l[qb] = 0.f;
 #pragma unroll
@@ -953,7 +1072,8 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
 #pragma unroll
       for (int i = 0; i < 16; ++i) ws.o[qb][db][i] = 0.f;
   }
-  wait_vmem();
+  if (pre > 0) wait_vmem_n<NST>();
+  else wait_vmem();
   __syncthreads();
 
   // Slots: group 0 runs M(i) in slot 2i and V(i) in slot 2i+1, group 1 one
@@ -1084,11 +1204,21 @@ __device__ __forceinline__ void process_item(const Params& p, const Copies<TL>& 
       __syncthreads();
     }
     merge_key_halves<TL>(ws, smem, grp, qw, lane);
-    if (grp == 1) return;
   }
-
-  store_output<T, TL>(p, ws, sp * p.o_split + b * p.o_sb + h * p.o_sh,
+  // Every ring read of this item is over (the barriers above), and Q is no
+  // longer needed: the next item's prologue goes out ahead of this item's
+  // stores.
+  int nxt = -1;
+  if (!CAUSAL && next >= 0) {
+    const ItemGeom gn = item_geom<TL, CAUSAL>(p, next, grp, qw, lr);
+    item_prologue<TL>(p, cp, gn, ring, ws, qw, lane);
+    nxt = 0;
+  }
+  if (KSPLIT && grp == 1) return nxt;  // group 0 stores the merged rows
+  store_output<T, TL>(p, ws, smem, sp * p.o_split + b * p.o_sb + h * p.o_sh,
                      sp * p.lse_split + (long long)bh * p.Sq, qt, qw, lane);
+  const bool full_rows = qt * TL::BM + (qw * QB + QB) * 32 <= p.Sq;  // wave-uniform
+  return nxt < 0 ? -1 : (full_rows ? NST : 0);
 }
 #undef ATTN_MPHASE
 #undef ATTN_VPHASE
@@ -1112,12 +1242,19 @@ void attn_fwd_kernel(Params p) {
   // with xcd_remap the items of one round are renumbered to give each XCD a
   // contiguous run of items, i.e. the query tiles of the same heads, whose
   // K/V then stay in that XCD's L2.
+  auto item_of = [&](int base) {
+    return p.xcd_remap ? base + (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3)
+                       : base + (int)blockIdx.x;
+  };
+  WaveState<TL> ws;
+  int pre = -1;
   for (int round = 0;; ++round) {
     const int base = round * G;
     if (base >= p.n_items) break;
-    int item = base + (int)blockIdx.x;
-    if (p.xcd_remap) item = base + (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
-    if (item < p.n_items) process_item<T, TL, CAUSAL>(p, cp, smem, item, wave, lane);
+    const int item = item_of(base);
+    const int next = (!CAUSAL && base + G < p.n_items && item_of(base + G) < p.n_items)
+                         ? item_of(base + G) : -1;
+    if (item < p.n_items) pre = process_item<T, TL, CAUSAL>(p, cp, smem, item, next, wave, lane, ws, pre);
   }
 }
 
