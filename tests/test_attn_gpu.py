@@ -308,6 +308,26 @@ def test_grid_sizes_give_identical_results():
         assert torch.equal(o, ref) and torch.equal(lse, ref_l), g
 
 
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "fp16"), (128, "fp16"), (64, "bf16")])
+def test_persistent_rounds_all_variants(D, dtype):
+    """Grids far below the item count, every tiling: each workgroup runs many
+    items in turn, ragged last query tiles among them.  On non-causal grids an
+    item issues the next item's first copies and Q rows ahead of its own
+    output stores, which go through LDS where the tiling has room for it."""
+    scale = 1 / math.sqrt(D)
+    q, k, v = W.gaussian_qkv(1, 3, 1111, D, dtype, seed=37)
+    ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale)
+    for var in variants_for(D, dtype):
+        for g in (1, 5):
+            say(f"rounds D={D} {dtype} variant {var} grid {g}")
+            o, lse = gpu_run(q, k, v, scale, variant=var, grid=g)
+            err = np.abs(o.cpu().to(torch.float64).numpy() - ro)
+            el = np.abs(lse.cpu().to(torch.float64).numpy() - rl)
+            say(f"  O max {err.max():.3e} mean {err.mean():.3e} LSE max {el.max():.3e}")
+            assert np.all(np.isfinite(err)) and np.all(np.isfinite(el))
+            assert err.max() <= O_MAX and err.mean() <= O_MEAN and el.max() <= LSE_MAX, (var, g)
+
+
 def test_non_default_stream():
     q, k, v = W.gaussian_qkv(1, 4, 512, 64, "fp16", seed=26)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
