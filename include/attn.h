@@ -248,8 +248,11 @@ int attn_merge(const float* o_parts, const float* lse_parts, int n_parts, void* 
  * associative, which is what licenses splitting the key axis across
  * workgroups; its References name split-KV as the split-K of that carrier.)
  *
- *   kv_splits        >= 1, or 0 for the library's choice (enough items to
- *                    fill every compute unit, each range at least 256 keys).
+ *   kv_splits        >= 1, or 0 for the library's choice: no split unless the
+ *                    items would fill at most half of the compute units,
+ *                    then up to one item per compute unit with ranges of at
+ *                    least 1024 keys (4096 where more than a quarter of the
+ *                    units would already be busy).
  *   workspace        device memory of at least
  *                    attn_fwd_split_workspace_size(B, H, S, D, kv_splits)
  *                    bytes, 256-byte aligned, owned by the caller; its

@@ -242,8 +242,8 @@ def test_split_validation_and_workspace_size(lib):
     l_bytes = n * B * H * S * 4
     up = lambda x: (x + 255) // 256 * 256
     assert lib.attn_fwd_split_workspace_size(B, H, S, D, n) == up(o_bytes) + up(l_bytes)
-    # automatic choice: sized for at most S / 256 ranges (capped at 64, at least 1)
-    assert lib.attn_fwd_split_workspace_size(1, 1, 4096, 64, 0) == up(16 * 4096 * 64 * 4) + up(16 * 4096 * 4)
+    # automatic choice: sized for at most S / 1024 ranges (capped at 64, at least 1)
+    assert lib.attn_fwd_split_workspace_size(1, 1, 4096, 64, 0) == up(4 * 4096 * 64 * 4) + up(4 * 4096 * 4)
     assert lib.attn_fwd_split_workspace_size(1, 1, 100, 64, 0) == up(100 * 64 * 4) + up(100 * 4)
     assert lib.attn_fwd_split_workspace_size(1, 1, 100, 96, 1) == 0
 
