@@ -3,8 +3,9 @@ CPU oracle.
 
 Each case draws a head size, dtype, batch and head counts, query and key
 lengths (equal or not, ragged or whole tiles), a causal mask (none, the default
-diagonal, or an explicit offset), BHSD or BSHD storage, a tile variant and a
-scale, and compares every output element.  Same bar as the other parity tests:
+diagonal, or an explicit offset), BHSD or BSHD storage, a tile variant, a
+scale and a grid size (the library's, or a few workgroups that each run many
+items in turn), and compares every output element.  Same bar as the other parity tests:
 max |dO| <= 2e-2, mean |dO| <= 2e-3 against the unrounded oracle, max |dLSE|
 <= 1e-3 (rows that see no key must give O = 0 and LSE = -inf on both sides).
 """
@@ -68,10 +69,12 @@ def _device_view(t, layout):
 
 def test_random_shapes_sweep():
     rng = np.random.default_rng(20261202)
+    grid_rng = np.random.default_rng(77)  # its own stream: the shapes stay as they were
     for n in range(N_CASES):
         D, dtype, B, H, Sq, Skv, causal, layout, variant, scale = _draw(rng)
+        grid = int(grid_rng.choice([0, 0, 1, 2, 5]))
         tag = (f"case {n}: B={B} H={H} Sq={Sq} Skv={Skv} D={D} {dtype} causal={causal} "
-               f"{layout} variant={variant} scale={scale:.4f}")
+               f"{layout} variant={variant} scale={scale:.4f} grid={grid}")
         say(tag)
         q, _, _ = W.gaussian_qkv(B, H, Sq, D, dtype, seed=3000 + n)
         _, k, v = W.gaussian_qkv(B, H, Skv, D, dtype, seed=4000 + n)
@@ -80,7 +83,8 @@ def test_random_shapes_sweep():
             od = torch.empty((B, Sq, H, D), dtype=q.dtype, device="cuda").transpose(1, 2)
         else:
             od = torch.empty((B, H, Sq, D), dtype=q.dtype, device="cuda")
-        o, lse = da.attn_fwd_strided(qd, kd, vd, od, scale=scale, variant=variant, causal=causal)
+        o, lse = da.attn_fwd_strided(qd, kd, vd, od, scale=scale, variant=variant, causal=causal,
+                                     grid=grid)
         torch.cuda.synchronize()
         offset = None if causal is False else (Skv - Sq if causal is True else causal)
         ro, rl = attention_forward(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale,
