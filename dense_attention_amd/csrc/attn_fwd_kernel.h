@@ -1014,8 +1014,8 @@ __device__ __forceinline__ int process_item(const Params& p, const Copies<TL>& c
                                             WaveState<TL>& ws, int pre) {
   constexpr int D = TL::D, BN = TL::BN, QB = TL::QB, DB = D / 32;
   constexpr bool KSPLIT = TL::KSPLIT;
-  // O stores of a wave whose rows are all below Sq (at least; more with fp32
-  // partials or the LSE).
+  // O store instructions of a wave whose rows are all below Sq, direct or
+  // staged through LDS (at least; more with fp32 partials or the LSE).
   constexpr int NST = QB * DB * 2;
   static_assert(!CAUSAL || QB == 1, "causal masks assume one 32-query block per wave");
   const int lr = lane & 31;
