@@ -302,3 +302,29 @@ def test_noalloc_refuses_partials_beyond_the_static_scratch(lib):
     text = open(HEADER).read()
     assert "#define ATTN_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)" in text
     assert da.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
+
+
+def test_plain_c_caller(tmp_path):
+    """The header compiles as strict C99 (and as C++) with warnings as errors,
+    and a C program linked against libattn.so runs the host-only calls and
+    the argument checks (tests/c_abi_check.c)."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    here = os.path.dirname(os.path.abspath(__file__))
+    inc = os.path.join(os.path.dirname(here), "include")
+    libdir = os.path.dirname(da.library_path())
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc,
+                    os.path.join(here, "c_abi_check.c"), "-o", exe, "-L", libdir, "-lattn",
+                    "-Wl,-rpath," + libdir], check=True, capture_output=True, text=True)
+    cxx = shutil.which("g++")
+    if cxx is not None:
+        src = tmp_path / "hdr.cpp"
+        src.write_text('#include "attn.h"\nint main() { return attn_variant_count() > 0 ? 0 : 1; }\n')
+        subprocess.run([cxx, "-std=c++11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc,
+                        "-c", str(src), "-o", str(tmp_path / "hdr.o")], check=True,
+                       capture_output=True, text=True)
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "c abi check ok" in run.stdout, run.stdout + run.stderr
