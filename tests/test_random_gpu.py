@@ -11,6 +11,7 @@ max |dO| <= 2e-2, mean |dO| <= 2e-3 against the unrounded oracle, max |dLSE|
 """
 
 import math
+import os
 import sys
 
 import numpy as np
@@ -24,7 +25,9 @@ from oracle import attention_forward
 pytestmark = pytest.mark.gpu
 
 O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
-N_CASES = 60
+# More cases or another draw on request: ATTN_RANDOM_CASES, ATTN_RANDOM_SEED.
+N_CASES = int(os.environ.get("ATTN_RANDOM_CASES", "60"))
+SEED = int(os.environ.get("ATTN_RANDOM_SEED", "20261202"))
 
 
 def say(msg):
@@ -68,7 +71,7 @@ def _device_view(t, layout):
 
 
 def test_random_shapes_sweep():
-    rng = np.random.default_rng(20261202)
+    rng = np.random.default_rng(SEED)
     grid_rng = np.random.default_rng(77)  # its own stream: the shapes stay as they were
     for n in range(N_CASES):
         D, dtype, B, H, Sq, Skv, causal, layout, variant, scale = _draw(rng)
